@@ -1,0 +1,213 @@
+/*
+ * stdspec.h -- C ABI of the MI355X (gfx950) Sparse-to-Dense decoding hot path.
+ *
+ * Source: "Sparse-to-Dense: A Free Lunch for Lossless Acceleration of Video
+ * Understanding in LLMs".  The pages describe StD as two modes of one model:
+ * a sparse model M_s that drafts gamma tokens with top-K attention over the
+ * visual KV chosen at prefill, and the dense model M that verifies them in
+ * one pass over the full KV cache, accepting the longest agreeing prefix and
+ * one bonus token (technical summary, Methodology items 2-4).
+ *
+ * Four calls make the hot path, all per layer (except accept), all
+ * asynchronous on the caller's HIP stream:
+ *   std_select_topk        prefill-time top-K visual KV selection
+ *   std_sparse_decode_attn draft-step attention over the selected KV
+ *   std_dense_verify_attn  verify attention of gamma+1 queries, full KV
+ *   std_accept             greedy longest-prefix acceptance + bonus token
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named q, k, v, out, logits, idx, ... are DEVICE pointers; the
+ *   shape structs are HOST pointers read during the call only.  The caller
+ *   owns every buffer.  The library allocates and frees nothing and keeps no
+ *   state between calls, so calls on different streams do not interfere
+ *   (except through buffers the caller shares between them).
+ * - KV cache of one layer: separate K and V, each [n_kv_heads][capacity]
+ *   [head_dim], row-major, dtype bf16 or fp32; positions [0, len) are valid.
+ * - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
+ * - Queries take the KV dtype; outputs are written in the KV dtype; all
+ *   accumulation is fp32 (selection scores accumulate across tiles in fp64).
+ * - scale multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ * - head_dim must be 64 or 128.
+ * - Argument checks run on the host before any launch; a failed check returns
+ *   a status and launches nothing.  STD_ERR_HIP reports a launch failure.
+ *   Device-side contents (idx inside the visual span, ascending, distinct)
+ *   are preconditions and are not checked.  Nothing prints or aborts.
+ * - stream is a hipStream_t passed as void*; NULL means the default stream.
+ * - Workspace: each call that needs scratch takes a caller-allocated device
+ *   buffer of at least the size its *_workspace query returns (256-byte
+ *   aligned).  Its contents need no initialisation and are garbage after
+ *   the call.  Two calls in flight at once need two workspaces.
+ */
+#ifndef STDSPEC_H
+#define STDSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STD_ABI_VERSION 1
+
+typedef enum {
+  STD_OK = 0,
+  STD_ERR_INVALID_ARGUMENT = 1,   /* a null pointer, a size out of range ...  */
+  STD_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. d=96)    */
+  STD_ERR_WORKSPACE_TOO_SMALL = 3,
+  STD_ERR_HIP = 4                 /* a HIP launch or runtime call failed      */
+} std_status_t;
+
+typedef enum { STD_DTYPE_F32 = 0, STD_DTYPE_BF16 = 1 } std_dtype_t;
+
+/* Attention shape of one layer. */
+typedef struct {
+  int32_t n_q_heads;   /* H_q >= 1                                    */
+  int32_t n_kv_heads;  /* H_kv >= 1, divides H_q                      */
+  int32_t head_dim;    /* d, 64 or 128                                */
+  float scale;         /* > 0, finite                                 */
+} std_attn_shape_t;
+
+/* One layer's KV cache (device pointers). */
+typedef struct {
+  const void* k;       /* [n_kv_heads][capacity][head_dim]            */
+  const void* v;       /* [n_kv_heads][capacity][head_dim]            */
+  int32_t capacity;    /* allocated positions per head                */
+  int32_t len;         /* valid positions, 1 <= len <= capacity       */
+  std_dtype_t dtype;
+} std_kv_t;
+
+/* The visual span [vis_start, vis_start + vis_len) of the cache. */
+typedef struct {
+  int32_t vis_start;
+  int32_t vis_len;
+} std_vis_t;
+
+/* ABI version the library was built with (STD_ABI_VERSION). */
+int32_t std_abi_version(void);
+
+/* Static string naming a status. */
+const char* std_status_str(std_status_t status);
+
+/* Human-readable reason for the last non-OK status returned on the calling
+ * thread (thread-local; "" if none).  Valid until the next call on it. */
+const char* std_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * (a) Prefill-time top-K visual KV selection.
+ *
+ * Technical summary, Methodology item 4 ("KV cache selection"): the top-K
+ * visual KV are chosen once, during prefill, from the average attention
+ * score directed from text tokens to visual tokens; the choice differs per
+ * layer and per attention head.  Item 2 names the basis: attention weights
+ * from text tokens to visual tokens.
+ *
+ * For each KV head g and visual position j:
+ *   score[g][j] = 1/(G*n_text) * sum_{h in group g} sum_{i < n_text}
+ *                 softmax_h,i(j)
+ * where softmax_h,i is the causal attention row of text query i of query
+ * head h, at position text_start + i, over every key it sees (positions
+ * [0, text_start + i]).  idx_out[g] receives the K positions with the
+ * largest scores, ties to the lower position, in ascending order.
+ *
+ * q_text   [n_q_heads][n_text][head_dim], KV dtype, the prefill's text
+ *          queries (already rotated if the model rotates them).
+ * kv       cache holding at least positions [0, text_start + n_text);
+ *          kv->len >= text_start + n_text.
+ * vis      visual span; vis_start + vis_len <= text_start (text follows the
+ *          visual span), vis_len >= 1.
+ * topk     1 <= topk <= vis_len.
+ * lse_or_null  optional [n_q_heads][n_text] fp32 natural-log log-sum-exp of
+ *          each text row (scale applied), e.g. from the caller's prefill
+ *          attention; when given the library skips computing it.
+ * idx_out  [n_kv_heads][topk] int32, absolute cache positions, ascending.
+ * scores_or_null  optional [n_kv_heads][vis_len] fp32 mean probabilities.
+ * ------------------------------------------------------------------------ */
+size_t std_select_topk_workspace(const std_attn_shape_t* shape, int32_t n_text,
+                                 std_vis_t vis, int32_t topk, const std_kv_t* kv);
+std_status_t std_select_topk(const std_attn_shape_t* shape, const void* q_text,
+                             int32_t text_start, int32_t n_text, const std_kv_t* kv,
+                             std_vis_t vis, int32_t topk, const float* lse_or_null,
+                             int32_t* idx_out, float* scores_or_null,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (b) Sparse draft attention, one query token.
+ *
+ * Technical summary, Methodology item 2: the sparse model M_s uses top-K
+ * attention over the visual KV chosen at prefill, cutting draft-phase I/O;
+ * item 3: it drafts gamma tokens autoregressively, one at a time.
+ *
+ * The query sits at position kv->len - 1.  Query head h (KV head g) attends
+ * with softmax over the positions
+ *   [0, vis_start)  +  idx[g][0..topk)  +  [vis_start + vis_len, kv->len)
+ * i.e. every non-visual position and the selected visual ones.
+ *
+ * q    [n_q_heads][head_dim], KV dtype.
+ * idx  [n_kv_heads][topk] int32 absolute positions inside the visual span,
+ *      distinct (as std_select_topk returns them); 0 <= topk <= vis_len.
+ * vis  the visual span lies inside the valid cache:
+ *      vis_start + vis_len <= kv->len; the key set must be non-empty.
+ * out  [n_q_heads][head_dim], KV dtype.
+ * ------------------------------------------------------------------------ */
+size_t std_sparse_decode_workspace(const std_attn_shape_t* shape, const std_kv_t* kv,
+                                   std_vis_t vis, int32_t topk);
+std_status_t std_sparse_decode_attn(const std_attn_shape_t* shape, const void* q,
+                                    const std_kv_t* kv, std_vis_t vis, const int32_t* idx,
+                                    int32_t topk, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (c) Dense verify attention: n_q queries, one pass over the full KV.
+ *
+ * Technical summary, Methodology item 2: the dense model M uses the full KV
+ * cache (standard attention); item 3: it verifies the gamma drafted tokens
+ * in parallel with a single I/O pass over the full KV cache.
+ *
+ * Query i (0 <= i < n_q) sits at position kv->len - n_q + i and attends
+ * causally to positions [0, kv->len - n_q + i].  With n_q = 1 this is plain
+ * dense decoding.  Each KV head is streamed from HBM once for all n_q*G of
+ * its query rows.  The split of the keys across workgroups depends only on
+ * kv->len, never on n_q.
+ *
+ * q    [n_q][n_q_heads][head_dim], KV dtype.   1 <= n_q <= kv->len.
+ * out  [n_q][n_q_heads][head_dim], KV dtype.
+ * ------------------------------------------------------------------------ */
+size_t std_dense_verify_workspace(const std_attn_shape_t* shape, int32_t n_q,
+                                  const std_kv_t* kv);
+std_status_t std_dense_verify_attn(const std_attn_shape_t* shape, const void* q,
+                                   int32_t n_q, const std_kv_t* kv, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (d) Greedy acceptance plus the bonus token.
+ *
+ * Technical summary, Methodology item 3: verification finds the longest
+ * prefix of drafted tokens matching the dense model's predictions (n
+ * tokens) and accepts one extra bonus token; the accepted tokens are
+ * appended to the context.
+ *
+ * pred[i] = argmax_v logits[i][v] (ties to the lowest id); row i is the
+ * dense prediction after the i-th verify input (x_t, d_1, ..., d_gamma).
+ * n = the largest n <= gamma with draft[j] == pred[j] for all j < n.
+ *
+ * draft        [gamma] int32 device; gamma >= 0 (gamma = 0: plain greedy).
+ * logits       [gamma+1][vocab] device, fp32 or bf16; vocab >= 1.
+ * out_tokens   [gamma+1] int32 device: pred[0..n] (= d_1..d_n, then the
+ *              bonus), -1 in the remaining slots.
+ * n_out        int32 device scalar: n + 1, in [1, gamma + 1].
+ * margins_or_null  [gamma+1] fp32 device: top1 - top2 of each row (0 on a
+ *              tie at the top).
+ * seq_len_inout_or_null  int32 device scalar; if given, n + 1 is added.
+ * ------------------------------------------------------------------------ */
+std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
+                        int32_t vocab, std_dtype_t logits_dtype, int32_t* out_tokens,
+                        int32_t* n_out, float* margins_or_null,
+                        int32_t* seq_len_inout_or_null, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STDSPEC_H */

@@ -1,0 +1,22 @@
+"""Sparse-to-Dense (StD) speculative decoding hot path for MI355X (gfx950).
+
+The four calls of the hot path are hand-written HIP kernels behind the C ABI
+of libstdspec.so (include/stdspec.h); this package is the thin Python
+binding over it (torch supplies device memory and the HIP stream):
+
+  std_select_topk         prefill-time top-K visual KV selection
+  std_sparse_decode_attn  sparse draft attention (one query token)
+  std_dense_verify_attn   dense verify attention (gamma+1 queries, full KV)
+  std_accept              greedy longest-prefix acceptance + bonus token
+
+Importing this package does not load the library; the first call does, and
+fails loudly if it has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    StdError, load, attn_shape, kv_desc,
+    std_select_topk, std_select_topk_workspace,
+    std_sparse_decode_attn, std_sparse_decode_workspace,
+    std_dense_verify_attn, std_dense_verify_workspace,
+    std_accept,
+)

@@ -1,0 +1,257 @@
+"""ctypes binding of libstdspec (the gfx950 HIP library); marshalling only.
+
+Each function has the name of the C entry point it wraps (include/stdspec.h),
+takes torch tensors that live on the GPU, passes their device pointers and
+torch's current HIP stream, and raises StdError on a non-OK status.  Every
+step of the computation runs in the HIP kernels; there is no fallback: if
+the library is missing, loading fails with an error.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstdspec.so")
+
+STD_OK = 0
+STD_ERR_INVALID_ARGUMENT = 1
+STD_ERR_UNSUPPORTED = 2
+STD_ERR_WORKSPACE_TOO_SMALL = 3
+STD_ERR_HIP = 4
+STD_DTYPE_F32 = 0
+STD_DTYPE_BF16 = 1
+
+
+class StdError(RuntimeError):
+    def __init__(self, status, name, detail):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("capacity", ctypes.c_int32), ("len", ctypes.c_int32),
+                ("dtype", ctypes.c_int)]
+
+
+class Vis(ctypes.Structure):
+    _fields_ = [("vis_start", ctypes.c_int32), ("vis_len", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "std_abi_version": (_I, []),
+    "std_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "std_last_error": (ctypes.c_char_p, []),
+    "std_dense_verify_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, ctypes.POINTER(KV)]),
+    "std_dense_verify_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I,
+                                             ctypes.POINTER(KV), _P, _P, _SZ, _P]),
+    "std_sparse_decode_workspace": (_SZ, [ctypes.POINTER(AttnShape), ctypes.POINTER(KV), Vis, _I]),
+    "std_sparse_decode_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, ctypes.POINTER(KV),
+                                              Vis, _P, _I, _P, _P, _SZ, _P]),
+    "std_select_topk_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, Vis, _I,
+                                        ctypes.POINTER(KV)]),
+    "std_select_topk": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
+                                       ctypes.POINTER(KV), Vis, _I, _P, _P, _P, _P, _SZ, _P]),
+    "std_accept": (ctypes.c_int, [_P, _I, _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libstdspec.so (built by sparse_draft_speculative_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m sparse_draft_speculative_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status, name):
+    if status != STD_OK:
+        lib = load()
+        raise StdError(status, lib.std_status_str(status).decode(),
+                       f"{name}: {lib.std_last_error().decode()}")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return STD_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return STD_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def attn_shape(n_q_heads, n_kv_heads, head_dim, scale=None):
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return AttnShape(n_q_heads, n_kv_heads, head_dim, scale)
+
+
+def kv_desc(k, v, length):
+    return KV(k.data_ptr() if k is not None else 0, v.data_ptr() if v is not None else 0,
+              k.shape[1], int(length), _dtype_code(k))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    return workspace
+
+
+# ----------------------------------------------------------------------------
+def std_dense_verify_workspace(shape, n_q, k, length):
+    return load().std_dense_verify_workspace(ctypes.byref(shape), int(n_q),
+                                             ctypes.byref(kv_desc(k, None, length)))
+
+
+def std_dense_verify_attn(q, k, v, length, out=None, scale=None, workspace=None, stream=None):
+    """Dense verify attention.  q [n_q][H_q][d]; k, v [H_kv][capacity][d]."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    n_q, hq, d = q.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, length)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    ws = _workspace(lib.std_dense_verify_workspace(ctypes.byref(shape), n_q, ctypes.byref(kv)),
+                    q.device, workspace)
+    _check(lib.std_dense_verify_attn(ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv),
+                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "std_dense_verify_attn")
+    return out
+
+
+def std_sparse_decode_workspace(shape, k, length, vis_start, vis_len, topk):
+    return load().std_sparse_decode_workspace(ctypes.byref(shape),
+                                              ctypes.byref(kv_desc(k, None, length)),
+                                              Vis(vis_start, vis_len), int(topk))
+
+
+def std_sparse_decode_attn(q, k, v, length, vis_start, vis_len, idx, out=None, scale=None,
+                           workspace=None, stream=None):
+    """Sparse draft attention.  q [H_q][d]; idx [H_kv][K] int32 (K may be 0)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx")):
+        _dev(t, n)
+    if idx.dtype != torch.int32:
+        raise ValueError("idx must be int32")
+    hq, d = q.shape
+    hkv = k.shape[0]
+    topk = idx.shape[1] if idx.dim() == 2 else 0
+    if idx.dim() != 2 or idx.shape[0] != hkv:
+        raise ValueError("idx must be [H_kv][K]")
+    shape = attn_shape(hq, hkv, d, scale)
+    kv = kv_desc(k, v, length)
+    vis = Vis(vis_start, vis_len)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    ws = _workspace(lib.std_sparse_decode_workspace(ctypes.byref(shape), ctypes.byref(kv), vis,
+                                                    topk), q.device, workspace)
+    _check(lib.std_sparse_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(kv), vis,
+                                      _ptr(idx), topk, _ptr(out), _ptr(ws), ws.numel(),
+                                      _stream(stream)),
+           "std_sparse_decode_attn")
+    return out
+
+
+def std_select_topk_workspace(shape, n_text, vis_start, vis_len, topk, k, length):
+    return load().std_select_topk_workspace(ctypes.byref(shape), int(n_text),
+                                            Vis(vis_start, vis_len), int(topk),
+                                            ctypes.byref(kv_desc(k, None, length)))
+
+
+def std_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, lse=None,
+                    idx_out=None, scores_out=None, scale=None, workspace=None, stream=None,
+                    want_scores=False):
+    """Top-K visual KV selection.  q_text [H_q][n_text][d]; k [H_kv][capacity][d].
+
+    Returns idx [H_kv][topk] int32 (and the fp32 scores if want_scores).
+    """
+    lib = load()
+    _dev(q_text, "q_text")
+    _dev(k, "k")
+    hq, n_text, d = q_text.shape
+    hkv = k.shape[0]
+    shape = attn_shape(hq, hkv, d, scale)
+    kv = kv_desc(k, k, length)
+    vis = Vis(vis_start, vis_len)
+    if idx_out is None:
+        idx_out = torch.empty(hkv, topk, dtype=torch.int32, device=k.device)
+    if scores_out is None and want_scores:
+        scores_out = torch.empty(hkv, vis_len, dtype=torch.float32, device=k.device)
+    if lse is not None:
+        _dev(lse, "lse")
+    ws = _workspace(lib.std_select_topk_workspace(ctypes.byref(shape), n_text, vis, topk,
+                                                  ctypes.byref(kv)), k.device, workspace)
+    _check(lib.std_select_topk(ctypes.byref(shape), _ptr(q_text), text_start, n_text,
+                               ctypes.byref(kv), vis, topk, _ptr(lse), _ptr(idx_out),
+                               _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "std_select_topk")
+    return (idx_out, scores_out) if want_scores else idx_out
+
+
+def std_accept(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len=None,
+               stream=None):
+    """Greedy acceptance.  draft [gamma] int32; logits [gamma+1][vocab].
+
+    Returns (out_tokens [gamma+1] int32, n_out [1] int32) on the device.
+    """
+    lib = load()
+    _dev(draft, "draft")
+    _dev(logits, "logits")
+    gamma = draft.numel()
+    vocab = logits.shape[1]
+    dev = logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty(gamma + 1, dtype=torch.int32, device=dev)
+    if n_out is None:
+        n_out = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.std_accept(_ptr(draft), gamma, _ptr(logits), vocab, _dtype_code(logits),
+                          _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len),
+                          _stream(stream)),
+           "std_accept")
+    return out_tokens, n_out

@@ -1,0 +1,109 @@
+// Greedy acceptance plus the bonus token (gfx950, wave64).
+//
+// Technical summary, Methodology item 3 ("decoding procedure"): verification
+// finds the longest prefix of drafted tokens matching the dense model's
+// predictions (n tokens) and accepts one extra bonus token; the accepted
+// tokens are appended to the context.
+//
+//  argmax_rows  -- one 256-thread workgroup per logit row: argmax (ties to
+//                  the lowest id) and margin = top1 - top2.  The prediction
+//                  is written straight into out_tokens[row].
+//  accept_commit -- one wave: n = length of the agreeing prefix, n_out = n+1,
+//                  slots after the bonus set to -1, optional seq_len += n+1.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace stdspec {
+namespace {
+
+struct Best {
+  float v;     // best value
+  int i;       // its id (lowest on ties)
+  float v2;    // best value among all other ids
+};
+
+__device__ __forceinline__ Best merge(Best a, Best b) {
+  const bool a_wins = a.v > b.v || (a.v == b.v && a.i < b.i);
+  Best r;
+  if (a_wins) { r.v = a.v; r.i = a.i; r.v2 = fmaxf(a.v2, b.v); }
+  else        { r.v = b.v; r.i = b.i; r.v2 = fmaxf(b.v2, a.v); }
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void argmax_rows(const T* __restrict__ logits, int vocab,
+                                                   int32_t* __restrict__ pred,
+                                                   float* __restrict__ margins) {
+  __shared__ Best sh[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const T* lr = logits + (size_t)row * vocab;
+  Best b{-INFINITY, 0x7fffffff, -INFINITY};
+  for (int j = tid; j < vocab; j += 256) {   // ids increase: first maximum wins
+    const float x = Elem<T>::load(lr, j);
+    if (x > b.v || b.i == 0x7fffffff) { b.v2 = fmaxf(b.v2, b.v); b.v = x; b.i = j; }
+    else b.v2 = fmaxf(b.v2, x);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    Best other;
+    other.v = __shfl_xor(b.v, o, kWave);
+    other.i = __shfl_xor(b.i, o, kWave);
+    other.v2 = __shfl_xor(b.v2, o, kWave);
+    b = merge(b, other);
+  }
+  if ((tid & 63) == 0) sh[tid >> 6] = b;
+  __syncthreads();
+  if (tid == 0) {
+    Best r = sh[0];
+    for (int w = 1; w < 4; ++w) r = merge(r, sh[w]);
+    pred[row] = r.i;
+    if (margins) margins[row] = vocab > 1 ? r.v - r.v2 : INFINITY;
+  }
+}
+
+__global__ __launch_bounds__(64) void accept_commit(const int32_t* __restrict__ draft, int gamma,
+                                                    int32_t* __restrict__ out_tokens,
+                                                    int32_t* __restrict__ n_out,
+                                                    int32_t* __restrict__ seq_len) {
+  __shared__ int sh_n;
+  const int lane = threadIdx.x;
+  if (lane == 0) sh_n = gamma;
+  __syncthreads();
+  // first j with draft[j] != pred[j] (pred lives in out_tokens)
+  for (int base = 0; base < gamma; base += 64) {
+    const int j = base + lane;
+    const bool miss = j < gamma && draft[j] != out_tokens[j];
+    const unsigned long long mask = __ballot(miss);
+    if (mask) {
+      if (lane == 0) sh_n = base + __ffsll((long long)mask) - 1;
+      break;
+    }
+  }
+  __syncthreads();
+  const int n = sh_n;
+  for (int j = n + 1 + lane; j <= gamma; j += 64) out_tokens[j] = -1;
+  if (lane == 0) {
+    n_out[0] = n + 1;
+    if (seq_len) seq_len[0] += n + 1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_accept(const int32_t* draft, int gamma, const void* logits, int vocab, bool bf16,
+                         int32_t* out_tokens, int32_t* n_out, float* margins, int32_t* seq_len,
+                         hipStream_t st) {
+  if (bf16)
+    argmax_rows<uint16_t><<<gamma + 1, 256, 0, st>>>(static_cast<const uint16_t*>(logits), vocab,
+                                                     out_tokens, margins);
+  else
+    argmax_rows<float><<<gamma + 1, 256, 0, st>>>(static_cast<const float*>(logits), vocab,
+                                                  out_tokens, margins);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  accept_commit<<<1, 64, 0, st>>>(draft, gamma, out_tokens, n_out, seq_len);
+  return hipGetLastError();
+}
+
+}  // namespace stdspec

@@ -1,0 +1,281 @@
+// C ABI of libstdspec: host-side argument checks, workspace sizing and
+// dispatch to the gfx950 kernels.  Declarations and their contracts are in
+// include/stdspec.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/stdspec.h"
+#include "internal.hpp"
+
+using namespace stdspec;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+std_status_t fail(std_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+std_status_t fail(std_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+std_status_t ok() {
+  g_err[0] = '\0';
+  return STD_OK;
+}
+
+std_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(STD_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+}
+
+#define CHECK(cond, st, ...) \
+  do {                       \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+std_status_t check_shape(const std_attn_shape_t* s) {
+  CHECK(s, STD_ERR_INVALID_ARGUMENT, "shape is null");
+  CHECK(s->n_q_heads >= 1 && s->n_kv_heads >= 1, STD_ERR_INVALID_ARGUMENT,
+        "head counts must be >= 1 (got %d, %d)", s->n_q_heads, s->n_kv_heads);
+  CHECK(s->n_q_heads % s->n_kv_heads == 0, STD_ERR_INVALID_ARGUMENT,
+        "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", s->n_q_heads, s->n_kv_heads);
+  CHECK(s->head_dim > 0, STD_ERR_INVALID_ARGUMENT, "head_dim must be positive");
+  CHECK(s->head_dim == 64 || s->head_dim == 128, STD_ERR_UNSUPPORTED,
+        "head_dim %d unsupported (64 or 128)", s->head_dim);
+  CHECK(isfinite(s->scale) && s->scale > 0.f, STD_ERR_INVALID_ARGUMENT,
+        "scale must be finite and > 0");
+  return ok();
+}
+
+std_status_t check_kv(const std_kv_t* kv, bool need_ptrs) {
+  CHECK(kv, STD_ERR_INVALID_ARGUMENT, "kv is null");
+  CHECK(kv->dtype == STD_DTYPE_F32 || kv->dtype == STD_DTYPE_BF16, STD_ERR_INVALID_ARGUMENT,
+        "unknown kv dtype %d", (int)kv->dtype);
+  CHECK(kv->capacity >= 1 && kv->len >= 1 && kv->len <= kv->capacity, STD_ERR_INVALID_ARGUMENT,
+        "need 1 <= len (%d) <= capacity (%d)", kv->len, kv->capacity);
+  if (need_ptrs) CHECK(kv->k && kv->v, STD_ERR_INVALID_ARGUMENT, "kv->k / kv->v is null");
+  return ok();
+}
+
+// Cache extent in elements must stay addressable with 32-bit row indices
+// multiplied out in 64-bit; reject absurd sizes early.
+std_status_t check_extent(const std_attn_shape_t* s, const std_kv_t* kv) {
+  const double elems = (double)s->n_kv_heads * kv->capacity * s->head_dim;
+  CHECK(elems < 9.0e15, STD_ERR_INVALID_ARGUMENT, "cache too large");
+  return ok();
+}
+
+#define TRY(expr)                            \
+  do {                                       \
+    std_status_t _st = (expr);               \
+    if (_st != STD_OK) return _st;           \
+  } while (0)
+
+std_status_t check_sparse(const std_attn_shape_t* s, const std_kv_t* kv, std_vis_t vis,
+                          int32_t topk) {
+  CHECK(vis.vis_start >= 0 && vis.vis_len >= 1, STD_ERR_INVALID_ARGUMENT,
+        "need vis_start >= 0 and vis_len >= 1");
+  CHECK((long long)vis.vis_start + vis.vis_len <= kv->len, STD_ERR_INVALID_ARGUMENT,
+        "visual span [%d, %lld) exceeds len %d", vis.vis_start,
+        (long long)vis.vis_start + vis.vis_len, kv->len);
+  CHECK(topk >= 0 && topk <= vis.vis_len, STD_ERR_INVALID_ARGUMENT,
+        "need 0 <= topk (%d) <= vis_len (%d)", topk, vis.vis_len);
+  CHECK(sparse_list_len(kv->len, vis.vis_start, vis.vis_len, topk) >= 1, STD_ERR_INVALID_ARGUMENT,
+        "the sparse key set is empty");
+  (void)s;
+  return ok();
+}
+
+int sparse_splits(const std_kv_t* kv, std_vis_t vis, int topk) {
+  const int L = sparse_list_len(kv->len, vis.vis_start, vis.vis_len, topk);
+  return (L + kSparseChunk - 1) / kSparseChunk;
+}
+
+int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int* chunk) {
+  *chunk = dense_chunk_keys(kv->len, s->n_kv_heads);
+  return (kv->len + *chunk - 1) / *chunk;
+}
+
+std_status_t check_ws(void* ws, size_t have, size_t need) {
+  CHECK(have >= need, STD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", have,
+        need);
+  CHECK(need == 0 || ws, STD_ERR_INVALID_ARGUMENT, "workspace is null");
+  CHECK(((uintptr_t)ws & 255) == 0, STD_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t std_abi_version(void) { return STD_ABI_VERSION; }
+
+const char* std_status_str(std_status_t st) {
+  switch (st) {
+    case STD_OK: return "STD_OK";
+    case STD_ERR_INVALID_ARGUMENT: return "STD_ERR_INVALID_ARGUMENT";
+    case STD_ERR_UNSUPPORTED: return "STD_ERR_UNSUPPORTED";
+    case STD_ERR_WORKSPACE_TOO_SMALL: return "STD_ERR_WORKSPACE_TOO_SMALL";
+    case STD_ERR_HIP: return "STD_ERR_HIP";
+  }
+  return "STD_ERR_UNKNOWN";
+}
+
+const char* std_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------- dense verify
+size_t std_dense_verify_workspace(const std_attn_shape_t* s, int32_t n_q, const std_kv_t* kv) {
+  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK || n_q < 1) return 0;
+  int chunk;
+  const int splits = dense_splits(s, kv, &chunk);
+  return split_workspace(splits, n_q * s->n_q_heads, s->head_dim).bytes();
+}
+
+std_status_t std_dense_verify_attn(const std_attn_shape_t* s, const void* q, int32_t n_q,
+                                   const std_kv_t* kv, void* out, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  TRY(check_shape(s));
+  TRY(check_kv(kv, true));
+  TRY(check_extent(s, kv));
+  CHECK(q && out, STD_ERR_INVALID_ARGUMENT, "q / out is null");
+  CHECK(n_q >= 1 && n_q <= kv->len, STD_ERR_INVALID_ARGUMENT, "need 1 <= n_q (%d) <= len (%d)",
+        n_q, kv->len);
+  CHECK((long long)n_q * s->n_q_heads <= (1 << 24), STD_ERR_INVALID_ARGUMENT,
+        "too many query rows");
+  CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
+        STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
+  int chunk;
+  const int splits = dense_splits(s, kv, &chunk);
+  const SplitWorkspace w = split_workspace(splits, n_q * s->n_q_heads, s->head_dim);
+  TRY(check_ws(ws, ws_bytes, w.bytes()));
+  AttnArgs a{};
+  a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
+  a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
+  a.capacity = kv->capacity; a.len = kv->len; a.n_q = n_q;
+  a.bf16 = kv->dtype == STD_DTYPE_BF16;
+  a.sparse = false;
+  a.ml = static_cast<float*>(ws);
+  a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(w.ml_bytes));
+  a.splits = splits; a.chunk = chunk;
+  return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- sparse draft
+size_t std_sparse_decode_workspace(const std_attn_shape_t* s, const std_kv_t* kv, std_vis_t vis,
+                                   int32_t topk) {
+  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK ||
+      check_sparse(s, kv, vis, topk) != STD_OK)
+    return 0;
+  return split_workspace(sparse_splits(kv, vis, topk), s->n_q_heads, s->head_dim).bytes();
+}
+
+std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
+                                    std_vis_t vis, const int32_t* idx, int32_t topk, void* out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_shape(s));
+  TRY(check_kv(kv, true));
+  TRY(check_extent(s, kv));
+  TRY(check_sparse(s, kv, vis, topk));
+  CHECK(q && out, STD_ERR_INVALID_ARGUMENT, "q / out is null");
+  CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
+  CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
+        STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
+  const int splits = sparse_splits(kv, vis, topk);
+  const SplitWorkspace w = split_workspace(splits, s->n_q_heads, s->head_dim);
+  TRY(check_ws(ws, ws_bytes, w.bytes()));
+  AttnArgs a{};
+  a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
+  a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
+  a.capacity = kv->capacity; a.len = kv->len; a.n_q = 1;
+  a.bf16 = kv->dtype == STD_DTYPE_BF16;
+  a.sparse = true; a.idx = idx;
+  a.vis_start = vis.vis_start; a.vis_len = vis.vis_len; a.topk = topk;
+  a.ml = static_cast<float*>(ws);
+  a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(w.ml_bytes));
+  a.splits = splits; a.chunk = kSparseChunk;
+  return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- selection
+static std_status_t check_select(const std_attn_shape_t* s, int32_t text_start, int32_t n_text,
+                                 const std_kv_t* kv, std_vis_t vis, int32_t topk) {
+  TRY(check_shape(s));
+  TRY(check_kv(kv, false));
+  CHECK(n_text >= 1, STD_ERR_INVALID_ARGUMENT, "n_text must be >= 1");
+  CHECK(vis.vis_start >= 0 && vis.vis_len >= 1, STD_ERR_INVALID_ARGUMENT,
+        "need vis_start >= 0 and vis_len >= 1");
+  CHECK((long long)vis.vis_start + vis.vis_len <= text_start, STD_ERR_INVALID_ARGUMENT,
+        "text rows must follow the visual span (text_start %d < vis_end %lld)", text_start,
+        (long long)vis.vis_start + vis.vis_len);
+  CHECK((long long)text_start + n_text <= kv->len, STD_ERR_INVALID_ARGUMENT,
+        "text rows [%d, %lld) exceed len %d", text_start, (long long)text_start + n_text,
+        kv->len);
+  CHECK(topk >= 1 && topk <= vis.vis_len, STD_ERR_INVALID_ARGUMENT,
+        "need 1 <= topk (%d) <= vis_len (%d)", topk, vis.vis_len);
+  CHECK((long long)s->n_q_heads * n_text <= (1 << 26), STD_ERR_INVALID_ARGUMENT,
+        "too many text rows");
+  return ok();
+}
+
+size_t std_select_topk_workspace(const std_attn_shape_t* s, int32_t n_text, std_vis_t vis,
+                                 int32_t topk, const std_kv_t* kv) {
+  if (!kv || check_shape(s) != STD_OK) return 0;
+  const int text_start = vis.vis_start + vis.vis_len;  // earliest legal start
+  const int ts = kv->len - n_text > text_start ? kv->len - n_text : text_start;
+  if (check_select(s, ts, n_text, kv, vis, topk) != STD_OK) return 0;
+  // size for the largest text_start the cache allows, so the value covers
+  // any call with this (shape, n_text, vis, topk, kv)
+  return select_workspace_bytes(s->n_q_heads, s->n_kv_heads, s->head_dim, n_text, vis.vis_len,
+                                kv->len - n_text, true);
+}
+
+std_status_t std_select_topk(const std_attn_shape_t* s, const void* q_text, int32_t text_start,
+                             int32_t n_text, const std_kv_t* kv, std_vis_t vis, int32_t topk,
+                             const float* lse_or_null, int32_t* idx_out, float* scores_or_null,
+                             void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_select(s, text_start, n_text, kv, vis, topk));
+  TRY(check_extent(s, kv));
+  CHECK(kv->k, STD_ERR_INVALID_ARGUMENT, "kv->k is null");
+  CHECK(q_text && idx_out, STD_ERR_INVALID_ARGUMENT, "q_text / idx_out is null");
+  CHECK(aligned16(q_text) && aligned16(kv->k), STD_ERR_INVALID_ARGUMENT,
+        "q_text, k must be 16-byte aligned");
+  const size_t need = select_workspace_bytes(s->n_q_heads, s->n_kv_heads, s->head_dim, n_text,
+                                             vis.vis_len, text_start, scores_or_null == nullptr);
+  TRY(check_ws(ws, ws_bytes, need));
+  SelectArgs a{};
+  a.q_text = q_text; a.k = kv->k;
+  a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
+  a.capacity = kv->capacity; a.text_start = text_start; a.n_text = n_text;
+  a.vis_start = vis.vis_start; a.vis_len = vis.vis_len; a.topk = topk;
+  a.bf16 = kv->dtype == STD_DTYPE_BF16;
+  a.lse_in = lse_or_null; a.idx_out = idx_out; a.scores_out = scores_or_null; a.ws = ws;
+  return hip_status(launch_select(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- acceptance
+std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits, int32_t vocab,
+                        std_dtype_t logits_dtype, int32_t* out_tokens, int32_t* n_out,
+                        float* margins_or_null, int32_t* seq_len_inout_or_null, void* stream) {
+  CHECK(gamma >= 0 && gamma < (1 << 20), STD_ERR_INVALID_ARGUMENT, "gamma %d out of range",
+        gamma);
+  CHECK(vocab >= 1, STD_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+  CHECK(gamma == 0 || draft, STD_ERR_INVALID_ARGUMENT, "draft is null");
+  CHECK(logits && out_tokens && n_out, STD_ERR_INVALID_ARGUMENT,
+        "logits / out_tokens / n_out is null");
+  CHECK(logits_dtype == STD_DTYPE_F32 || logits_dtype == STD_DTYPE_BF16,
+        STD_ERR_INVALID_ARGUMENT, "unknown logits dtype %d", (int)logits_dtype);
+  return hip_status(launch_accept(draft, gamma, logits, vocab, logits_dtype == STD_DTYPE_BF16,
+                                  out_tokens, n_out, margins_or_null, seq_len_inout_or_null,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

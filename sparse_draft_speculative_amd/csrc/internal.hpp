@@ -1,0 +1,109 @@
+// Host-side declarations shared by the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace stdspec {
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int pow2_floor(long long x) {
+  int p = 1;
+  while ((long long)p * 2 <= x) p *= 2;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K geometry.
+//
+// Dense verify: keys [0, len) are cut into fixed chunks of kc positions,
+// chunk c = [c*kc, (c+1)*kc).  kc depends only on (len, n_kv_heads) so the
+// same key is always reduced in the same chunk whatever n_q is; a power of
+// two between 128 and 2048 chosen so one layer launches about 512 chunks.
+inline int dense_chunk_keys(int len, int n_kv_heads) {
+  long long want = (long long)len * n_kv_heads / 512;
+  int kc = pow2_floor(want < 1 ? 1 : want);
+  if (kc < 128) kc = 128;
+  if (kc > 2048) kc = 2048;
+  return kc;
+}
+
+// Sparse decode: the per-head key list (prefix + selected + tail) is cut
+// into chunks of 64 entries, one wave each.
+constexpr int kSparseChunk = 64;
+
+inline int sparse_list_len(int len, int vis_start, int vis_len, int topk) {
+  return vis_start + topk + (len - (vis_start + vis_len));
+}
+
+struct SplitWorkspace {
+  int splits;     // number of key chunks
+  int rows;       // query rows = n_q * n_q_heads
+  int head_dim;
+  size_t ml_bytes, o_bytes;
+  size_t bytes() const { return align256(ml_bytes) + align256(o_bytes); }
+};
+
+inline SplitWorkspace split_workspace(int splits, int rows, int head_dim) {
+  SplitWorkspace w;
+  w.splits = splits;
+  w.rows = rows;
+  w.head_dim = head_dim;
+  w.ml_bytes = (size_t)splits * rows * 2 * sizeof(float);
+  w.o_bytes = (size_t)splits * rows * head_dim * sizeof(float);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (attention.hip).  All return the hipError_t of the launch.
+
+struct AttnArgs {
+  const void* q;        // dense: [n_q][Hq][D]; sparse: [Hq][D]
+  const void* k;
+  const void* v;
+  void* out;
+  int hq, hkv, d;
+  float scale;
+  int capacity, len, n_q;
+  bool bf16;
+  // sparse key list; for dense, sparse == false
+  bool sparse;
+  const int32_t* idx;
+  int vis_start, vis_len, topk;
+  // workspace
+  float* ml;            // [splits][rows][2]
+  float* o;             // [splits][rows][D]
+  int splits;
+  int chunk;            // keys (dense) or list entries (sparse) per split
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+// Selection (select.hip).
+struct SelectArgs {
+  const void* q_text;   // [Hq][n_text][D]
+  const void* k;        // [Hkv][capacity][D]
+  int hq, hkv, d;
+  float scale;
+  int capacity;
+  int text_start, n_text;
+  int vis_start, vis_len, topk;
+  bool bf16;
+  const float* lse_in;  // optional natural-log LSE [Hq][n_text]
+  int32_t* idx_out;
+  float* scores_out;    // [Hkv][vis_len] (caller's or workspace)
+  void* ws;
+};
+
+size_t select_workspace_bytes(int hq, int hkv, int d, int n_text, int vis_len,
+                              int text_start, bool scores_in_ws);
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+// Acceptance (accept.hip).
+hipError_t launch_accept(const int32_t* draft, int gamma, const void* logits, int vocab,
+                         bool bf16, int32_t* out_tokens, int32_t* n_out, float* margins,
+                         int32_t* seq_len, hipStream_t stream);
+
+}  // namespace stdspec

@@ -1,0 +1,153 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any launch.
+
+Every call below passes a null workspace of 0 bytes, so even a call whose
+other arguments were accepted would stop at the workspace check and could
+never launch a kernel.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_draft_speculative_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stdspec.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libstdspec.so not built")
+
+FAKE = 0x10000       # a 16-byte aligned non-null address; never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(std_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    names = declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib._SIGS), "binding and header disagree"
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.std_abi_version() == 1
+    assert lib.std_status_str(0) == b"STD_OK"
+    assert lib.std_status_str(3) == b"STD_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.std_status_str(99) == b"STD_ERR_UNKNOWN"
+
+
+def _shape(hq=28, hkv=4, d=128, scale=0.088):
+    return _lib.AttnShape(hq, hkv, d, scale)
+
+
+def _kv(cap=1000, length=900, dtype=_lib.STD_DTYPE_BF16, k=FAKE, v=FAKE):
+    return _lib.KV(k, v, cap, length, dtype)
+
+
+def _dense(shape, n_q=6, kv=None, q=FAKE, out=FAKE):
+    lib = _lib.load()
+    kv = kv or _kv()
+    return lib.std_dense_verify_attn(ctypes.byref(shape), ctypes.c_void_p(q), n_q,
+                                     ctypes.byref(kv), ctypes.c_void_p(out), None, 0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(shape=_shape(hq=28, hkv=5)), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(d=96)), _lib.STD_ERR_UNSUPPORTED),
+    (dict(shape=_shape(scale=0.0)), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(scale=float("nan"))), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), n_q=0), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), n_q=901), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), kv=_kv(length=1001)), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), kv=_kv(k=0)), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), kv=_kv(dtype=7)), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), q=0), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), q=FAKE + 2), _lib.STD_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape()), _lib.STD_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_dense_verify_rejects(kwargs, status):
+    assert _dense(**kwargs) == status
+    assert _lib.load().std_last_error() != b""
+
+
+def test_sparse_decode_rejects():
+    lib = _lib.load()
+    sh = _shape()
+
+    def call(vis=(0, 800), topk=64, idx=FAKE, kv=None):
+        kv = kv or _kv()
+        return lib.std_sparse_decode_attn(ctypes.byref(sh), ctypes.c_void_p(FAKE), ctypes.byref(kv),
+                                          _lib.Vis(*vis), ctypes.c_void_p(idx), topk,
+                                          ctypes.c_void_p(FAKE), None, 0, None)
+
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    assert call(topk=801) == E                 # K > vis_len
+    assert call(topk=-1) == E
+    assert call(vis=(0, 901)) == E             # span beyond len
+    assert call(vis=(-1, 10)) == E
+    assert call(idx=0) == E                    # K > 0 needs idx
+    assert call(vis=(0, 900), topk=0) == E     # empty key set
+    assert call() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert call(topk=0, idx=0) == _lib.STD_ERR_WORKSPACE_TOO_SMALL   # K = 0 is legal
+
+
+def test_select_rejects():
+    lib = _lib.load()
+    sh = _shape()
+
+    def call(text_start=800, n_text=64, vis=(0, 800), topk=128, kv=None):
+        kv = kv or _kv()
+        return lib.std_select_topk(ctypes.byref(sh), ctypes.c_void_p(FAKE), text_start, n_text,
+                                   ctypes.byref(kv), _lib.Vis(*vis), topk, None,
+                                   ctypes.c_void_p(FAKE), None, None, 0, None)
+
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    assert call(text_start=799) == E           # text must follow the visual span
+    assert call(n_text=0) == E
+    assert call(n_text=101) == E               # beyond len 900
+    assert call(topk=0) == E
+    assert call(topk=801) == E
+    assert call() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_accept_rejects():
+    lib = _lib.load()
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    p = ctypes.c_void_p(FAKE)
+    assert lib.std_accept(p, -1, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept(p, 3, p, 0, 0, p, p, None, None, None) == E
+    assert lib.std_accept(None, 3, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept(p, 3, None, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept(p, 3, p, 10, 5, p, p, None, None, None) == E
+
+
+def test_workspace_sizes():
+    lib = _lib.load()
+    sh = _shape()
+    small = lib.std_dense_verify_workspace(ctypes.byref(sh), 7, ctypes.byref(_kv(200000, 142055)))
+    big = lib.std_dense_verify_workspace(ctypes.byref(sh), 7, ctypes.byref(_kv(300000, 284110)))
+    assert 0 < small <= big
+    # chunking depends on len only: n_q scales the rows linearly
+    one = lib.std_dense_verify_workspace(ctypes.byref(sh), 1, ctypes.byref(_kv(200000, 142055)))
+    assert one < small
+    assert lib.std_dense_verify_workspace(ctypes.byref(sh), 0, ctypes.byref(_kv())) == 0
+    s1 = lib.std_sparse_decode_workspace(ctypes.byref(sh), ctypes.byref(_kv(200000, 142049)),
+                                         _lib.Vis(0, 140000), 4096)
+    s2 = lib.std_sparse_decode_workspace(ctypes.byref(sh), ctypes.byref(_kv(200000, 142049)),
+                                         _lib.Vis(0, 140000), 8192)
+    assert 0 < s1 < s2
+    w = lib.std_select_topk_workspace(ctypes.byref(sh), 2048, _lib.Vis(0, 140000), 4096,
+                                      ctypes.byref(_kv(142048, 142048)))
+    assert w >= 4 * 140000 * 4                 # room for the scores
+    assert lib.std_select_topk_workspace(ctypes.byref(sh), 2048, _lib.Vis(0, 140000), 0,
+                                         ctypes.byref(_kv(142048, 142048))) == 0

@@ -1,0 +1,285 @@
+"""GPU parity: every call of the HIP library against the float64 oracle.
+
+Inputs are seeded synthetic tensors (synth); the oracle reads back exactly
+the values the GPU received.  Bars: attention max-abs <= 2e-2 (bf16 KV) and
+<= 1e-5 (fp32 KV); top-K sets exact except for positions whose oracle score
+lies within 1e-6 relative of the K-th value (ties to the lower position);
+acceptance bit-exact.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_draft_speculative_amd as sd
+    sd.load()
+    return sd
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def layer(cfg, i=0):
+    return synth.attention_layer(cfg, i, device="cuda")
+
+
+def oracle_idx(cfg, lay):
+    idx, scores = oracle.select_topk(f64(lay["q_text"]), f64(lay["k"]), cfg.text_start,
+                                     cfg.vis_start, cfg.vis_len, cfg.topk)
+    return idx, scores
+
+
+def check_topk(gpu_idx, ref_scores, topk, vis_start, vis_len, band=1e-6):
+    """A15: distinct in-span ascending positions; the symmetric difference with
+    the oracle set lies in the 1e-6 band around the oracle's K-th score."""
+    gpu_idx = np.asarray(gpu_idx)
+    for g in range(gpu_idx.shape[0]):
+        sel = gpu_idx[g] - vis_start
+        assert len(set(sel.tolist())) == topk
+        assert np.all(np.diff(sel) > 0), "not ascending"
+        assert sel.min() >= 0 and sel.max() < vis_len
+        s = ref_scores[g]
+        ref = set(oracle.rank_topk(s, topk).tolist())
+        kth = np.sort(s)[::-1][topk - 1]
+        diff = ref.symmetric_difference(set(sel.tolist()))
+        bad = [j for j in diff if abs(s[j] - kth) > band * kth]
+        assert not bad, f"head {g}: {len(bad)} positions outside the tie band, e.g. {bad[:5]}"
+
+
+# ---------------------------------------------------------------- dense verify
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_dense_verify_matches_oracle(lib, name):
+    cfg = synth.config(name)
+    lay = layer(cfg)
+    say(f"dense verify {name} n_q={cfg.gamma + 1} len={cfg.verify_len}")
+    out = lib.std_dense_verify_attn(lay["q_verify"], lay["k"], lay["v"], cfg.verify_len)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify(f64(lay["q_verify"]), f64(lay["k"]), f64(lay["v"]), cfg.verify_len)
+    err = max_abs(f64(out), ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_dense_single_query_decode(lib, name):
+    cfg = synth.config(name)
+    lay = layer(cfg)
+    for j in (0, cfg.gamma - 1):
+        length = cfg.draft_len(j)
+        q = lay["q_draft"][j:j + 1].contiguous()
+        out = lib.std_dense_verify_attn(q, lay["k"], lay["v"], length)
+        torch.cuda.synchronize()
+        ref = oracle.dense_verify(f64(q), f64(lay["k"]), f64(lay["v"]), length)
+        assert max_abs(f64(out), ref) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype,n_q,length,cap", [
+    (8, 2, 64, "bf16", 7, 8390, 8400),      # toy-decoder shape, ragged length
+    (28, 4, 128, "bf16", 1, 65, 70),        # tiny cache, single query
+    (28, 4, 128, "bf16", 100, 3000, 3001),  # many query rows: several 64-row blocks
+    (4, 4, 64, "f32", 3, 777, 800),         # G = 1, fp32
+    (32, 1, 128, "bf16", 5, 4097, 4100),    # G = 32
+    (6, 2, 128, "f32", 2, 130, 130),
+])
+def test_dense_verify_shapes(lib, hq, hkv, d, dtype, n_q, length, cap):
+    g = torch.Generator(device="cuda").manual_seed(hq * 1000 + length)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    k = torch.randn(hkv, cap, d, generator=g, device="cuda").to(dt)
+    v = torch.randn(hkv, cap, d, generator=g, device="cuda").to(dt)
+    q = (torch.randn(n_q, hq, d, generator=g, device="cuda") * 1.5).to(dt)
+    say(f"dense shape hq={hq} hkv={hkv} d={d} {dtype} n_q={n_q} len={length}")
+    out = lib.std_dense_verify_attn(q, k, v, length)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify(f64(q), f64(k), f64(v), length)
+    assert max_abs(f64(out), ref) <= TOL[dtype]
+
+
+def test_dense_verify_is_deterministic_and_row_invariant(lib):
+    cfg = synth.config("c2")
+    lay = layer(cfg)
+    a = lib.std_dense_verify_attn(lay["q_verify"], lay["k"], lay["v"], cfg.verify_len)
+    b = lib.std_dense_verify_attn(lay["q_verify"], lay["k"], lay["v"], cfg.verify_len)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # the last verify row is the dense n_q=1 decode at the same length
+    one = lib.std_dense_verify_attn(lay["q_verify"][-1:].contiguous(), lay["k"], lay["v"],
+                                    cfg.verify_len)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], a[-1])
+
+
+# ---------------------------------------------------------------- sparse draft
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_sparse_decode_matches_oracle(lib, name):
+    cfg = synth.config(name)
+    lay = layer(cfg)
+    idx_ref, _ = oracle_idx(cfg, lay)
+    idx = torch.from_numpy(idx_ref.astype(np.int32)).cuda()
+    kf, vf = f64(lay["k"]), f64(lay["v"])
+    for j in range(cfg.gamma):
+        length = cfg.draft_len(j)
+        q = lay["q_draft"][j].contiguous()
+        say(f"sparse {name} step {j} len={length} K={cfg.topk}")
+        out = lib.std_sparse_decode_attn(q, lay["k"], lay["v"], length, cfg.vis_start,
+                                         cfg.vis_len, idx)
+        torch.cuda.synchronize()
+        ref = oracle.sparse_decode(f64(q), kf, vf, length, cfg.vis_start, cfg.vis_len, idx_ref)
+        err = max_abs(f64(out), ref)
+        assert err <= TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_sparse_full_selection_equals_dense(lib, name):
+    """K = vis_len: the sparse kernel must equal dense attention (oracle)."""
+    cfg = synth.config(name)
+    lay = layer(cfg)
+    hkv = cfg.n_kv_heads
+    idx = torch.arange(cfg.vis_start, cfg.vis_end, dtype=torch.int32, device="cuda")
+    idx = idx.repeat(hkv, 1).contiguous()
+    length = cfg.draft_len(0)
+    q = lay["q_draft"][0].contiguous()
+    out = lib.std_sparse_decode_attn(q, lay["k"], lay["v"], length, cfg.vis_start, cfg.vis_len, idx)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify(f64(q)[None], f64(lay["k"]), f64(lay["v"]), length)[0]
+    assert max_abs(f64(out), ref) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype,prefix,vis_len,length,topk", [
+    (28, 4, 128, "bf16", 0, 16384, 16897, 0),       # K = 0: text only
+    (28, 4, 128, "bf16", 37, 5000, 5100, 1),        # prefix before the span, K = 1
+    (8, 2, 64, "bf16", 5, 8192, 8330, 512),         # toy-decoder shape
+    (32, 2, 128, "bf16", 0, 1000, 1100, 100),       # G = 16
+    (34, 2, 128, "bf16", 0, 1000, 1100, 100),       # G = 17: vector-ALU path
+    (4, 1, 64, "f32", 10, 1000, 1200, 77),
+    (7, 7, 128, "f32", 0, 300, 301, 300),           # G = 1, K = vis_len
+])
+def test_sparse_decode_shapes(lib, hq, hkv, d, dtype, prefix, vis_len, length, topk):
+    gen = torch.Generator(device="cpu").manual_seed(hq * 7 + topk)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    cap = length + 3
+    k = torch.randn(hkv, cap, d, generator=gen).to(dt).cuda()
+    v = torch.randn(hkv, cap, d, generator=gen).to(dt).cuda()
+    q = (torch.randn(hq, d, generator=gen) * 1.5).to(dt).cuda()
+    idx_np = np.stack([np.sort(torch.randperm(vis_len, generator=gen)[:topk].numpy()) + prefix
+                       for _ in range(hkv)]).astype(np.int32).reshape(hkv, topk)
+    idx = torch.from_numpy(idx_np).cuda()
+    say(f"sparse shape hq={hq} hkv={hkv} d={d} {dtype} prefix={prefix} K={topk} len={length}")
+    out = lib.std_sparse_decode_attn(q, k, v, length, prefix, vis_len, idx)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_decode(f64(q), f64(k), f64(v), length, prefix, vis_len, idx_np)
+    assert max_abs(f64(out), ref) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------- selection
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_select_topk_matches_oracle(lib, name):
+    cfg = synth.config(name)
+    lay = layer(cfg)
+    say(f"select {name} n_text={cfg.n_text} vis={cfg.vis_len} K={cfg.topk}")
+    idx, scores = lib.std_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
+                                      cfg.vis_start, cfg.vis_len, cfg.topk, want_scores=True)
+    torch.cuda.synchronize()
+    _, ref_scores = oracle_idx(cfg, lay)
+    rel = np.abs(f64(scores) - ref_scores) / ref_scores
+    say(f"  score rel err max {rel.max():.2e} median {np.median(rel):.2e}")
+    assert rel.max() < 1e-4
+    check_topk(idx.cpu().numpy(), ref_scores, cfg.topk, cfg.vis_start, cfg.vis_len)
+
+
+def test_select_topk_exact_ties_and_prefix(lib):
+    """Duplicated key rows tie bitwise and the lower position wins; a
+    non-visual prefix before the span; bf16 d=64."""
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    hq, hkv, d, prefix, vis_len, n_text = 8, 2, 64, 9, 700, 40
+    cap = prefix + vis_len + n_text
+    k = torch.randn(hkv, cap, d, generator=gen)
+    q = torch.randn(hq, n_text, d, generator=gen)
+    u = torch.randn(d, generator=gen)
+    u /= u.norm()
+    q += 2 * u
+    for j in (50, 51, 400, 401, 402):
+        k[:, prefix + j] = 6 * u + k[:, prefix + 3]     # five copies of one strong row
+    k[:, prefix + 3] = 6 * u + k[:, prefix + 3]
+    q, k = q.bfloat16(), k.bfloat16()
+    for topk in (1, 3, 6, 7, vis_len):
+        idx, scores = lib.std_select_topk(q.cuda(), k.cuda(), cap, prefix + vis_len, prefix,
+                                          vis_len, topk, want_scores=True)
+        torch.cuda.synchronize()
+        sc = scores.cpu()
+        for g in range(hkv):
+            assert sc[g, 3] == sc[g, 50] == sc[g, 401], "identical rows must tie bitwise"
+        ref_idx, ref_scores = oracle.select_topk(f64(q), f64(k), prefix + vis_len, prefix,
+                                                 vis_len, topk)
+        check_topk(idx.cpu().numpy(), ref_scores, topk, prefix, vis_len)
+        if topk <= 6:
+            want = [prefix + j for j in (3, 50, 51, 400, 401, 402)][:topk]
+            assert ref_idx.tolist() == [want] * hkv          # premise of the case
+            assert idx.cpu().numpy().tolist() == [want] * hkv
+
+
+def test_select_topk_uses_caller_lse(lib):
+    cfg = synth.config("c1")
+    lay = layer(cfg)
+    # the natural-log LSE of each text row, from the oracle's definition
+    qf, kf = f64(lay["q_text"]), f64(lay["k"])
+    lse = np.empty((cfg.n_q_heads, cfg.n_text))
+    for h in range(cfg.n_q_heads):
+        for i in range(cfg.n_text):
+            s = (kf[0, : cfg.text_start + i + 1] @ qf[h, i]) / np.sqrt(cfg.head_dim)
+            lse[h, i] = s.max() + np.log(np.exp(s - s.max()).sum())
+    lse_t = torch.from_numpy(lse.astype(np.float32)).cuda()
+    idx, scores = lib.std_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
+                                      cfg.vis_start, cfg.vis_len, cfg.topk, lse=lse_t,
+                                      want_scores=True)
+    torch.cuda.synchronize()
+    _, ref_scores = oracle_idx(cfg, lay)
+    assert np.max(np.abs(f64(scores) - ref_scores) / ref_scores) < 1e-4
+    check_topk(idx.cpu().numpy(), ref_scores, cfg.topk, cfg.vis_start, cfg.vis_len)
+
+
+# ---------------------------------------------------------------- acceptance
+@pytest.mark.parametrize("gamma,vocab,dtype,agree,ties", [
+    (0, 8192, torch.float32, 0.9, 0),
+    (4, 8192, torch.float32, 0.95, 0),
+    (6, 8192, torch.bfloat16, 0.95, 2),
+    (9, 300, torch.float32, 1.0, 3),
+    (6, 152064, torch.bfloat16, 0.5, 1),
+    (70, 1000, torch.float32, 0.99, 0),
+    (5, 1, torch.float32, 1.0, 0),
+])
+def test_accept_matches_oracle(lib, gamma, vocab, dtype, agree, ties):
+    for seed in range(4):
+        draft, logits = synth.accept_case(gamma, vocab, agree, seed, dtype=dtype, n_ties=ties)
+        seq = torch.tensor([1000], dtype=torch.int32, device="cuda")
+        margins = torch.empty(gamma + 1, dtype=torch.float32, device="cuda")
+        out, n_out = lib.std_accept(draft.cuda(), logits.cuda(), margins=margins, seq_len=seq)
+        torch.cuda.synchronize()
+        ref_out, ref_n, ref_m, _ = oracle.accept(draft.numpy(), f64(logits))
+        assert out.cpu().numpy().tolist() == ref_out.tolist()
+        assert int(n_out.item()) == ref_n
+        assert int(seq.item()) == 1000 + ref_n
+        assert np.allclose(margins.cpu().numpy(), ref_m, rtol=1e-6, atol=1e-6)
