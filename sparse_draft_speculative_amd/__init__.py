@@ -19,4 +19,6 @@ from ._lib import (  # noqa: F401
     std_sparse_decode_attn, std_sparse_decode_workspace,
     std_dense_verify_attn, std_dense_verify_workspace,
     std_accept,
+    PreparedCall, prepare_dense_verify, prepare_sparse_decode, prepare_select_topk,
+    prepare_accept,
 )

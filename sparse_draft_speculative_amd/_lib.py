@@ -255,3 +255,73 @@ def std_accept(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len
                           _stream(stream)),
            "std_accept")
     return out_tokens, n_out
+
+
+# ----------------------------------------------------------------------------
+# Prepared calls: the argument tuple is built once, so a repeated call (the
+# decode loop issues a few hundred per cycle) costs one ctypes call.  Only
+# the valid cache length changes between calls; it lives in the KV struct.
+
+class PreparedCall:
+    def __init__(self, name, args, kv=None, keep=()):
+        self.name = name
+        self.fn = getattr(load(), name)
+        self.args = args
+        self.kv = kv
+        self._keep = keep           # keep ctypes structs and tensors alive
+
+    def __call__(self, length=None):
+        if length is not None:
+            self.kv.len = int(length)
+        st = self.fn(*self.args)
+        if st != STD_OK:
+            _check(st, self.name)
+
+
+def prepare_dense_verify(q, k, v, out, workspace, stream=None, scale=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (workspace, "workspace")):
+        _dev(t, n)
+    n_q, hq, d = q.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, k.shape[1])
+    args = (ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv), _ptr(out), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    return PreparedCall("std_dense_verify_attn", args, kv, (shape, kv, q, k, v, out, workspace))
+
+
+def prepare_sparse_decode(q, k, v, vis_start, vis_len, idx, out, workspace, stream=None,
+                          scale=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (out, "out"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    hq, d = q.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, k.shape[1])
+    args = (ctypes.byref(shape), _ptr(q), ctypes.byref(kv), Vis(vis_start, vis_len), _ptr(idx),
+            idx.shape[1], _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall("std_sparse_decode_attn", args, kv,
+                        (shape, kv, q, k, v, idx, out, workspace))
+
+
+def prepare_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, idx_out,
+                        workspace, scores_out=None, lse=None, stream=None, scale=None):
+    for t, n in ((q_text, "q_text"), (k, "k"), (idx_out, "idx_out"), (workspace, "workspace")):
+        _dev(t, n)
+    hq, n_text, d = q_text.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, k, length)
+    args = (ctypes.byref(shape), _ptr(q_text), text_start, n_text, ctypes.byref(kv),
+            Vis(vis_start, vis_len), topk, _ptr(lse), _ptr(idx_out), _ptr(scores_out),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall("std_select_topk", args, kv,
+                        (shape, kv, q_text, k, idx_out, workspace, scores_out, lse))
+
+
+def prepare_accept(draft, logits, out_tokens, n_out, margins=None, seq_len=None, stream=None):
+    for t, n in ((draft, "draft"), (logits, "logits"), (out_tokens, "out_tokens"),
+                 (n_out, "n_out")):
+        _dev(t, n)
+    args = (_ptr(draft), draft.numel(), _ptr(logits), logits.shape[1], _dtype_code(logits),
+            _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len), _stream(stream))
+    return PreparedCall("std_accept", args, None,
+                        (draft, logits, out_tokens, n_out, margins, seq_len))

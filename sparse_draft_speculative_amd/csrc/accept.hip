@@ -5,7 +5,7 @@
 // predictions (n tokens) and accepts one extra bonus token; the accepted
 // tokens are appended to the context.
 //
-//  argmax_rows  -- one 256-thread workgroup per logit row: argmax (ties to
+//  argmax_rows  -- one 1024-thread workgroup per logit row: argmax (ties to
 //                  the lowest id) and margin = top1 - top2.  The prediction
 //                  is written straight into out_tokens[row].
 //  accept_commit -- one wave: n = length of the agreeing prefix, n_out = n+1,
@@ -31,18 +31,44 @@ __device__ __forceinline__ Best merge(Best a, Best b) {
   return r;
 }
 
+constexpr int kArgmaxThreads = 1024;
+
+__device__ __forceinline__ void consider(Best& b, float x, int j) {
+  // elements reach a thread in increasing id order: the first maximum wins
+  if (x > b.v || b.i == 0x7fffffff) { b.v2 = fmaxf(b.v2, b.v); b.v = x; b.i = j; }
+  else b.v2 = fmaxf(b.v2, x);
+}
+
+// One workgroup per logit row.  Rows whose length is a multiple of 8 are read
+// with 16-byte loads (8 ids per thread per step), others element by element.
 template <typename T>
-__global__ __launch_bounds__(256) void argmax_rows(const T* __restrict__ logits, int vocab,
-                                                   int32_t* __restrict__ pred,
-                                                   float* __restrict__ margins) {
-  __shared__ Best sh[4];
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T* __restrict__ logits,
+                                                              int vocab,
+                                                              int32_t* __restrict__ pred,
+                                                              float* __restrict__ margins) {
+  __shared__ Best sh[kArgmaxThreads / kWave];
   const int row = blockIdx.x, tid = threadIdx.x;
   const T* lr = logits + (size_t)row * vocab;
   Best b{-INFINITY, 0x7fffffff, -INFINITY};
-  for (int j = tid; j < vocab; j += 256) {   // ids increase: first maximum wins
-    const float x = Elem<T>::load(lr, j);
-    if (x > b.v || b.i == 0x7fffffff) { b.v2 = fmaxf(b.v2, b.v); b.v = x; b.i = j; }
-    else b.v2 = fmaxf(b.v2, x);
+  constexpr int kVec = 16 / sizeof(T);                 // ids per 16-byte load
+  const bool vec = (vocab % 8) == 0 && (reinterpret_cast<uintptr_t>(lr) & 15) == 0;
+  if (vec) {
+    const int nchunk = vocab / kVec;
+#pragma unroll 4
+    for (int c = tid; c < nchunk; c += kArgmaxThreads) {
+      const uint4 u = *reinterpret_cast<const uint4*>(lr + (size_t)c * kVec);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          consider(b, bf16_bits_to_f32((w[e / 2] >> (16 * (e & 1))) & 0xffffu), c * 8 + e);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) consider(b, __uint_as_float(w[e]), c * 4 + e);
+      }
+    }
+  } else {
+    for (int j = tid; j < vocab; j += kArgmaxThreads) consider(b, Elem<T>::load(lr, j), j);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -56,7 +82,7 @@ __global__ __launch_bounds__(256) void argmax_rows(const T* __restrict__ logits,
   __syncthreads();
   if (tid == 0) {
     Best r = sh[0];
-    for (int w = 1; w < 4; ++w) r = merge(r, sh[w]);
+    for (int w = 1; w < kArgmaxThreads / kWave; ++w) r = merge(r, sh[w]);
     pred[row] = r.i;
     if (margins) margins[row] = vocab > 1 ? r.v - r.v2 : INFINITY;
   }
@@ -95,10 +121,10 @@ hipError_t launch_accept(const int32_t* draft, int gamma, const void* logits, in
                          int32_t* out_tokens, int32_t* n_out, float* margins, int32_t* seq_len,
                          hipStream_t st) {
   if (bf16)
-    argmax_rows<uint16_t><<<gamma + 1, 256, 0, st>>>(static_cast<const uint16_t*>(logits), vocab,
+    argmax_rows<uint16_t><<<gamma + 1, kArgmaxThreads, 0, st>>>(static_cast<const uint16_t*>(logits), vocab,
                                                      out_tokens, margins);
   else
-    argmax_rows<float><<<gamma + 1, 256, 0, st>>>(static_cast<const float*>(logits), vocab,
+    argmax_rows<float><<<gamma + 1, kArgmaxThreads, 0, st>>>(static_cast<const float*>(logits), vocab,
                                                   out_tokens, margins);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

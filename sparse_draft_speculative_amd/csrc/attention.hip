@@ -174,35 +174,37 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(
   const uint16_t* vh = v + (size_t)g * capacity * D;
   const int cv = tid % CPR, kg = tid / CPR;
 
-  uint4 kreg[KPT], vreg[KPT];
-  auto load_tile = [&](int t0) {
+  // Two register staging buffers: while tile t is reduced from LDS, tiles
+  // t+1 and t+2 are in flight from HBM.
+  uint4 kA[KPT], vA[KPT], kB[KPT], vB[KPT];
+  auto load_tile = [&](uint4* kr, uint4* vr, int t0) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int cl = tid + 256 * u;
       const int key = t0 + cl / CPR;
-      kreg[u] = key < key1 ? *reinterpret_cast<const uint4*>(kh + (size_t)key * D + (cl % CPR) * 8)
-                           : make_uint4(0, 0, 0, 0);
+      kr[u] = key < key1 ? *reinterpret_cast<const uint4*>(kh + (size_t)key * D + (cl % CPR) * 8)
+                         : make_uint4(0, 0, 0, 0);
       const int vkey = t0 + KPT * kg + u;
-      vreg[u] = vkey < key1 ? *reinterpret_cast<const uint4*>(vh + (size_t)vkey * D + cv * 8)
-                            : make_uint4(0, 0, 0, 0);
+      vr[u] = vkey < key1 ? *reinterpret_cast<const uint4*>(vh + (size_t)vkey * D + cv * 8)
+                          : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const uint4* kr, const uint4* vr) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int cl = tid + 256 * u;
-      *reinterpret_cast<uint4*>(Ks + (cl / CPR) * KP + (cl % CPR) * 8) = kreg[u];
+      *reinterpret_cast<uint4*>(Ks + (cl / CPR) * KP + (cl % CPR) * 8) = kr[u];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint16_t* dst = Vt + (cv * 8 + j) * VP + KPT * kg;
       if constexpr (KPT == 4) {
         uint2 w;
-        w.x = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
-        w.y = half16(vreg[2], j) | (half16(vreg[3], j) << 16);
+        w.x = half16(vr[0], j) | (half16(vr[1], j) << 16);
+        w.y = half16(vr[2], j) | (half16(vr[3], j) << 16);
         *reinterpret_cast<uint2*>(dst) = w;
       } else {
-        *reinterpret_cast<uint32_t*>(dst) = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
+        *reinterpret_cast<uint32_t*>(dst) = half16(vr[0], j) | (half16(vr[1], j) << 16);
       }
     }
   };
@@ -213,14 +215,13 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = (key1 - key0 + 63) / 64;
-  load_tile(key0);
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](uint4* kr, uint4* vr, int t) {
     const int t0 = key0 + t * 64;
     __syncthreads();
-    store_tile();
+    store_tile(kr, vr);
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t0 + 64);
-    if (!wave_active) continue;
+    if (t + 2 < ntiles) load_tile(kr, vr, t0 + 128);
+    if (!wave_active) return;
     floatx4_t sacc[4];
     TM::scores(Ks, qb, col, grp, sacc);
     float x[16], p[16];
@@ -235,6 +236,12 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(
     }
     online_update<DB>(x, p, m, lsum, oacc);
     TM::pv(Vt, p, col, grp, oacc);
+  };
+  load_tile(kA, vA, key0);
+  if (ntiles > 1) load_tile(kB, vB, key0 + 64);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(kA, vA, t);
+    if (t + 1 < ntiles) step(kB, vB, t + 1);
   }
 
   if (!wave_active) return;
@@ -409,23 +416,92 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Split combine: out[r] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <typename T>
-__global__ void combine_kernel(const float2* __restrict__ ml, const float* __restrict__ o,
-                               int splits, int rows, int D, T* __restrict__ out) {
-  const int r = blockIdx.x;
-  const int d = threadIdx.x;
+// Split combine: out[r] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// M = max_s m_s.  One 256-thread workgroup per query row; the splits are
+// spread over the threads (weights staged in LDS), each thread then sums a
+// float4 column over a strided subset of splits and the subsets are added
+// in a fixed order, so the result does not depend on timing.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineMaxSplits = 4096;   // LDS weights; larger S loops in chunks
+
+template <typename T, int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float2* __restrict__ ml, const float* __restrict__ o, int splits, int rows,
+    T* __restrict__ out) {
+  constexpr int DQ = D / 4;                      // float4 columns
+  constexpr int NSG = kCombineThreads / DQ;      // split groups
+  __shared__ float wsh[kCombineMaxSplits];
+  __shared__ float red[kCombineThreads / kWave];
+  __shared__ float4 part[NSG][DQ];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(size_t)s * rows + r].x);
+  for (int s = tid; s < splits; s += kCombineThreads) M = fmaxf(M, ml[(size_t)s * rows + r].x);
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / kWave; ++w) M = fmaxf(M, red[w]);
   const float Ms = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float2 st = ml[(size_t)s * rows + r];
-    const float w = fast_exp2(st.x - Ms);
-    L = fmaf(st.y, w, L);
-    acc = fmaf(w, o[((size_t)s * rows + r) * D + d], acc);
+  __syncthreads();
+
+  const int dq = tid % DQ, sg = tid / DQ;
+  float Lloc = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < splits; s0 += kCombineMaxSplits) {
+    const int s1 = min(splits, s0 + kCombineMaxSplits);
+    for (int s = s0 + tid; s < s1; s += kCombineThreads) {
+      const float2 st = ml[(size_t)s * rows + r];
+      const float w = fast_exp2(st.x - Ms);
+      wsh[s - s0] = w;
+      Lloc = fmaf(st.y, w, Lloc);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int s = s0 + sg; s < s1; s += NSG) {
+      const float w = wsh[s - s0];
+      const float4 x = *reinterpret_cast<const float4*>(o + ((size_t)s * rows + r) * D + 4 * dq);
+      acc.x = fmaf(w, x.x, acc.x);
+      acc.y = fmaf(w, x.y, acc.y);
+      acc.z = fmaf(w, x.z, acc.z);
+      acc.w = fmaf(w, x.w, acc.w);
+    }
+    __syncthreads();
   }
-  if (d < D) Elem<T>::store(out, (size_t)r * D + d, acc / L);
+  Lloc = wave_sum(Lloc);
+  if (lane == 0) red[wave] = Lloc;
+  part[sg][dq] = acc;
+  __syncthreads();
+  if (tid < DQ) {
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombineThreads / kWave; ++w) L += red[w];
+    float4 a = part[0][tid];
+#pragma unroll
+    for (int g = 1; g < NSG; ++g) {
+      const float4 b = part[g][tid];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    const float inv = 1.f / L;
+    const size_t base = (size_t)r * D + 4 * tid;
+    Elem<T>::store(out, base + 0, a.x * inv);
+    Elem<T>::store(out, base + 1, a.y * inv);
+    Elem<T>::store(out, base + 2, a.z * inv);
+    Elem<T>::store(out, base + 3, a.w * inv);
+  }
+}
+
+template <typename T>
+hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
+  const int rows = a.n_q * a.hq;
+  const auto* mlp = reinterpret_cast<const float2*>(a.ml);
+  T* out = static_cast<T*>(a.out);
+  if (a.d == 128)
+    combine_kernel<T, 128><<<rows, kCombineThreads, 0, st>>>(mlp, a.o, a.splits, rows, out);
+  else
+    combine_kernel<T, 64><<<rows, kCombineThreads, 0, st>>>(mlp, a.o, a.splits, rows, out);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -480,15 +556,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
                        : launch_valu<float, 64>(a, kl, n_entries, st);
   }
   if (err != hipSuccess) return err;
-  const int rows = a.n_q * a.hq;
-  const auto* mlp = reinterpret_cast<const float2*>(a.ml);
-  if (a.bf16)
-    combine_kernel<uint16_t><<<rows, a.d, 0, st>>>(mlp, a.o, a.splits, rows, a.d,
-                                                   static_cast<uint16_t*>(a.out));
-  else
-    combine_kernel<float><<<rows, a.d, 0, st>>>(mlp, a.o, a.splits, rows, a.d,
-                                                static_cast<float*>(a.out));
-  return hipGetLastError();
+  return a.bf16 ? launch_combine<uint16_t>(a, st) : launch_combine<float>(a, st);
 }
 
 }  // namespace stdspec

@@ -18,15 +18,17 @@ inline int pow2_floor(long long x) {
 // ---------------------------------------------------------------------------
 // Split-K geometry.
 //
-// Dense verify: keys [0, len) are cut into fixed chunks of kc positions,
-// chunk c = [c*kc, (c+1)*kc).  kc depends only on (len, n_kv_heads) so the
-// same key is always reduced in the same chunk whatever n_q is; a power of
-// two between 128 and 2048 chosen so one layer launches about 512 chunks.
+// Dense verify: keys [0, len) are cut into chunks of kc positions, chunk c
+// = [c*kc, (c+1)*kc), one workgroup each.  kc depends only on (len,
+// n_kv_heads), never on n_q, so a query row sees the same chunks and the
+// same reduction order whatever the number of rows in the call.  kc is a
+// multiple of 64 (the tile) sized so one layer launches about 512
+// workgroups: two resident per CU on 256 CUs, i.e. a single round.
 inline int dense_chunk_keys(int len, int n_kv_heads) {
-  long long want = (long long)len * n_kv_heads / 512;
-  int kc = pow2_floor(want < 1 ? 1 : want);
+  const int target = n_kv_heads >= 512 ? 1 : 512 / n_kv_heads;
+  int kc = (len + target - 1) / target;
+  kc = ((kc + 63) / 64) * 64;
   if (kc < 128) kc = 128;
-  if (kc > 2048) kc = 2048;
   return kc;
 }
 

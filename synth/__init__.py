@@ -47,6 +47,7 @@ class AttnConfig:
     planted: tuple             # ("count", n) | ("frac", f) | ("frac_u", lo, hi) | ("runs", run, f)
     seed: int = 0
     prefix: int = 0            # non-visual positions before the visual span
+    extra: int = 0             # further cache positions after ctx+gamma+1 (decode growth)
 
     @property
     def vis_start(self):
@@ -66,7 +67,7 @@ class AttnConfig:
 
     @property
     def capacity(self):
-        return self.ctx + self.gamma + 1
+        return self.ctx + self.gamma + 1 + self.extra
 
     @property
     def verify_len(self):
