@@ -22,7 +22,8 @@
 // 32-key step; no shuffle is needed between the two products.  Both
 // products contract over a permuted index (d, then keys) that is applied
 // identically to both operands, so the sums are unchanged.  V^T for the A
-// operand is produced by transposing V while staging it into LDS.
+// operand is read from the row-major V tile in LDS with the gfx950
+// transpose read (ds_read_b64_tr_b16), so V is staged without reshuffling.
 // Softmax runs in base 2 with the scale folded into one multiply.
 
 #include "common.hpp"
@@ -43,28 +44,41 @@ struct KeyList {
   }
 };
 
-__device__ __forceinline__ uint32_t half16(const uint4& r, int j) {
-  const uint32_t w = (j < 2) ? r.x : (j < 4) ? r.y : (j < 6) ? r.z : r.w;
-  return (j & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 __device__ __forceinline__ floatx4_t mfma_bf16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One 64-key tile of the online softmax for one wave's 16 query columns.
-//   Ks: [64][KP] keys (row-major), Vt: [D][VP] transposed values.
-//   x[kb*4+i] receives the scaled scores of keys kb*16 + 4*grp + i (already
-//   masked by the caller through ``valid``).
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group the lanes' 8-byte rows form
+// M[16][4]; lane i receives {M[4j + i/4][i%4] : j = 0..3}.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, t);
+}
+
+// LDS tile of 64 K or V rows, row-major, each 16-byte chunk of row r stored
+// at chunk slot (chunk ^ (r % CPR)) so the 16 rows touched by one MFMA
+// operand read fall in distinct banks.
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static __device__ __forceinline__ int off(int row, int chunk) {   // elements
+    return row * D + ((chunk ^ (row % CPR)) << 3);
+  }
+};
+
+// One 64-key tile for one wave's 16 query columns.
 template <int D>
 struct TileMath {
   static constexpr int KST = D / 32;   // 32-wide contraction steps over d
   static constexpr int DB = D / 16;    // 16-wide output blocks over d
-  static constexpr int KP = D + 8;     // LDS pitch of a K row (elements)
-  static constexpr int VP = 64 + 8;    // LDS pitch of a V^T row (elements)
 
+  // S^T = K Q^T for the 4 key blocks: lane (col, grp) gets keys
+  // kb*16 + 4*grp + i of query column col.
   static __device__ __forceinline__ void scores(const uint16_t* Ks, const bf16x8_t* qb,
                                                 int col, int grp, floatx4_t* sacc) {
 #pragma unroll
@@ -73,16 +87,21 @@ struct TileMath {
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         const uint4 a = *reinterpret_cast<const uint4*>(
-            Ks + (kb * 16 + col) * KP + (D / 4) * grp + 8 * kk);
+            Ks + Tile<D>::off(kb * 16 + col, KST * grp + kk));
         acc = mfma_bf16(as_bf16x8(a), qb[kk], acc);
       }
       sacc[kb] = acc;
     }
   }
 
-  // p holds 16 probabilities in (kb, i) order; accumulate O^T += V^T P^T.
-  static __device__ __forceinline__ void pv(const uint16_t* Vt, const float* p, int col,
+  // O^T += V^T P^T over the tile's 64 keys in two 32-key steps.  The B
+  // operand holds the lane's own probabilities (keys 32ks + 4grp + j and
+  // 32ks + 16 + 4grp + j); the A operand (V^T, lane = d row) is read from the
+  // row-major V tile with two transpose reads whose per-lane row addresses
+  // follow the same key order.
+  static __device__ __forceinline__ void pv(const uint16_t* Vs, const float* p, int col,
                                             int grp, floatx4_t* oacc) {
+    const int r4 = col >> 2, rc = col & 3;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 pw;
@@ -91,41 +110,49 @@ struct TileMath {
       pw.z = pack_bf16x2(p[(2 * ks + 1) * 4 + 0], p[(2 * ks + 1) * 4 + 1]);
       pw.w = pack_bf16x2(p[(2 * ks + 1) * 4 + 2], p[(2 * ks + 1) * 4 + 3]);
       const bf16x8_t pb = as_bf16x8(pw);
+      const int row0 = 32 * ks + 4 * grp + r4;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vr = Vt + (db * 16 + col) * VP + 32 * ks + 4 * grp;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        const int chunk = 2 * db + (rc >> 1);
+        const int e = 4 * (rc & 1);
+        const uint2 lo = lds_read_tr16(Vs + Tile<D>::off(row0, chunk) + e);
+        const uint2 hi = lds_read_tr16(Vs + Tile<D>::off(row0 + 16, chunk) + e);
         oacc[db] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, oacc[db]);
       }
     }
   }
 };
 
-// Online-softmax state update for one tile.  x: 16 scaled scores (-inf when
-// masked).  Returns probabilities in p; updates m (column max, identical in
-// the four lanes of a column), lsum (this lane's partial sum) and oacc.
+// Online softmax for one tile: x holds 16 base-2 scores (-inf when masked).
+// The running max m of a column moves only when a score exceeds it by more
+// than 2^8 (or m is unset); probabilities are taken relative to m, so they
+// stay below 256 and the accumulator rescale (AGPR round trips) is skipped
+// on almost every tile.  Exact: m is only a shift of the exponent.
+constexpr float kLazyMax = 8.f;
+
 template <int DB>
 __device__ __forceinline__ void online_update(const float* x, float* p, float& m, float& lsum,
                                               floatx4_t* oacc) {
-  float tmax = -INFINITY;
+  float tmax = x[0];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
+  for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-  const float mnew = fmaxf(m, tmax);
-  const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-  const float alpha = fast_exp2(m - msafe);
+  if (tmax > m + kLazyMax) {            // also taken while m is still -inf
+    const float alpha = fast_exp2(m - tmax);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    m = tmax;
+  }
+  const float msafe = (m == -INFINITY) ? 0.f : m;
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     p[j] = fast_exp2(x[j] - msafe);
     psum += p[j];
   }
-  lsum = lsum * alpha + psum;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-  m = mnew;
+  lsum += psum;
 }
 
 template <int D>
@@ -139,19 +166,76 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, bool ok, in
   }
 }
 
+// Move one 64-row tile of K and V: global -> registers (rows clamped to
+// the last valid one) and registers -> LDS (swizzled chunk slots).
+template <int D, int KPT>
+__device__ __forceinline__ void stage_load(u32x4_t (&kr)[KPT], u32x4_t (&vr)[KPT],
+                                           const uint16_t* kh, const uint16_t* vh, int t0,
+                                           int key1, const int (&rrow)[KPT],
+                                           const int (&rslot)[KPT]) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int key = min(t0 + rrow[u], key1 - 1);
+    const size_t off = (size_t)key * D + ((rslot[u] ^ (rrow[u] % CPR)) << 3);
+    kr[u] = *reinterpret_cast<const u32x4_t*>(kh + off);
+    vr[u] = *reinterpret_cast<const u32x4_t*>(vh + off);
+  }
+}
+
+template <int D, int KPT>
+__device__ __forceinline__ void stage_store(const u32x4_t (&kr)[KPT], const u32x4_t (&vr)[KPT],
+                                            uint16_t* ks, uint16_t* vs, const int (&rrow)[KPT],
+                                            const int (&rslot)[KPT]) {
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    *reinterpret_cast<u32x4_t*>(ks + rrow[u] * D + (rslot[u] << 3)) = kr[u];
+    *reinterpret_cast<u32x4_t*>(vs + rrow[u] * D + (rslot[u] << 3)) = vr[u];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Dense verify: grid (key chunk, KV head, 64-row block), 256 threads.
+//
+// Pipeline per 64-key tile t (one barrier per tile): tile t+1 is written
+// from registers into the other LDS buffer while tile t is reduced, and the
+// loads of tiles t+2 and t+3 are in flight in two more register buffers.
+// Loads are branch-free: rows past the chunk end are clamped to the last
+// valid row (finite data, masked out of the softmax).
+// Reduce one 64-key tile of LDS buffer ``buf`` into the wave's softmax state.
+template <int D>
+__device__ __forceinline__ void dense_tile(const uint16_t* Ks, const uint16_t* Vs,
+                                           const bf16x8_t* qb, int t0, int key1, int safe_end,
+                                           int qpos, float c, int col, int grp, float& m,
+                                           float& lsum, floatx4_t* oacc) {
+  using TM = TileMath<D>;
+  floatx4_t sacc[4];
+  TM::scores(Ks, qb, col, grp, sacc);
+  float x[16], p[16];
+  if (t0 + 64 <= safe_end) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = sacc[j >> 2][j & 3] * c;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = t0 + (j >> 2) * 16 + 4 * grp + (j & 3);
+      x[j] = (key < key1 && key <= qpos) ? sacc[j >> 2][j & 3] * c : -INFINITY;
+    }
+  }
+  online_update<TM::DB>(x, p, m, lsum, oacc);
+  TM::pv(Vs, p, col, grp, oacc);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void dense_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, int len, int n_q, float c,
     int chunk, float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
-  using TM = TileMath<D>;
-  constexpr int KP = TM::KP, VP = TM::VP, DB = TM::DB;
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int KPT = D / 32;    // K chunks per thread == V keys per thread
-  __shared__ __align__(16) uint16_t Ks[64 * KP];
-  __shared__ __align__(16) uint16_t Vt[D * VP];
+  constexpr int DB = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int KPT = 64 * CPR / 256;   // 16-byte chunks per thread per tensor
+  __shared__ __align__(16) uint16_t Ks[2][64 * D];
+  __shared__ __align__(16) uint16_t Vs[2][64 * D];
 
   const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -170,78 +254,56 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(
 
   const int key0 = s * chunk;
   const int key1 = min(len, key0 + chunk);
+  const int safe_end = min(key1, len - n_q + 1);   // keys < safe_end: visible to every row
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
-  const int cv = tid % CPR, kg = tid / CPR;
 
-  // Two register staging buffers: while tile t is reduced from LDS, tiles
-  // t+1 and t+2 are in flight from HBM.
-  uint4 kA[KPT], vA[KPT], kB[KPT], vB[KPT];
-  auto load_tile = [&](uint4* kr, uint4* vr, int t0) {
+  // thread -> (row, slot) of each chunk it moves; global chunk = slot ^ (row % CPR)
+  int rrow[KPT], rslot[KPT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cl = tid + 256 * u;
-      const int key = t0 + cl / CPR;
-      kr[u] = key < key1 ? *reinterpret_cast<const uint4*>(kh + (size_t)key * D + (cl % CPR) * 8)
-                         : make_uint4(0, 0, 0, 0);
-      const int vkey = t0 + KPT * kg + u;
-      vr[u] = vkey < key1 ? *reinterpret_cast<const uint4*>(vh + (size_t)vkey * D + cv * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](const uint4* kr, const uint4* vr) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cl = tid + 256 * u;
-      *reinterpret_cast<uint4*>(Ks + (cl / CPR) * KP + (cl % CPR) * 8) = kr[u];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint16_t* dst = Vt + (cv * 8 + j) * VP + KPT * kg;
-      if constexpr (KPT == 4) {
-        uint2 w;
-        w.x = half16(vr[0], j) | (half16(vr[1], j) << 16);
-        w.y = half16(vr[2], j) | (half16(vr[3], j) << 16);
-        *reinterpret_cast<uint2*>(dst) = w;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = half16(vr[0], j) | (half16(vr[1], j) << 16);
-      }
-    }
-  };
+  for (int u = 0; u < KPT; ++u) {
+    const int cl = tid + 256 * u;
+    rrow[u] = cl / CPR;
+    rslot[u] = cl % CPR;
+  }
 
   float m = -INFINITY, lsum = 0.f;
   floatx4_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Pipeline per 64-key tile t (one barrier per tile): tile t+1 moves from
+  // registers into the other LDS buffer while tile t is reduced, and tiles
+  // t+2, t+3 are in flight from HBM in two more register buffers.  Loads
+  // and stores are unconditional (tiles past the chunk re-read its last
+  // row), so the number of loads in flight is the same on every path and
+  // the compiler waits only for the buffer it is about to store.  The loop
+  // is unrolled by three so the three register buffers stay static.
   const int ntiles = (key1 - key0 + 63) / 64;
-  auto step = [&](uint4* kr, uint4* vr, int t) {
-    const int t0 = key0 + t * 64;
+  u32x4_t ka[KPT], va[KPT], kb_[KPT], vb[KPT], kc[KPT], vc[KPT];
+  stage_load<D, KPT>(ka, va, kh, vh, key0, key1, rrow, rslot);
+  stage_load<D, KPT>(kb_, vb, kh, vh, key0 + 64, key1, rrow, rslot);
+  stage_load<D, KPT>(kc, vc, kh, vh, key0 + 128, key1, rrow, rslot);
+  stage_store<D, KPT>(ka, va, Ks[0], Vs[0], rrow, rslot);
+  for (int t = 0; t < ntiles; t += 3) {
     __syncthreads();
-    store_tile(kr, vr);
+    stage_store<D, KPT>(kb_, vb, Ks[1], Vs[1], rrow, rslot);
+    stage_load<D, KPT>(ka, va, kh, vh, key0 + (t + 3) * 64, key1, rrow, rslot);
+    if (wave_active)
+      dense_tile<D>(Ks[0], Vs[0], qb, key0 + t * 64, key1, safe_end, qpos, c, col, grp, m, lsum,
+                    oacc);
     __syncthreads();
-    if (t + 2 < ntiles) load_tile(kr, vr, t0 + 128);
-    if (!wave_active) return;
-    floatx4_t sacc[4];
-    TM::scores(Ks, qb, col, grp, sacc);
-    float x[16], p[16];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = t0 + kb * 16 + 4 * grp + i;
-        const bool ok = key < key1 && key <= qpos;
-        x[kb * 4 + i] = ok ? sacc[kb][i] * c : -INFINITY;
-      }
-    }
-    online_update<DB>(x, p, m, lsum, oacc);
-    TM::pv(Vt, p, col, grp, oacc);
-  };
-  load_tile(kA, vA, key0);
-  if (ntiles > 1) load_tile(kB, vB, key0 + 64);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(kA, vA, t);
-    if (t + 1 < ntiles) step(kB, vB, t + 1);
+    stage_store<D, KPT>(kc, vc, Ks[0], Vs[0], rrow, rslot);
+    stage_load<D, KPT>(kb_, vb, kh, vh, key0 + (t + 4) * 64, key1, rrow, rslot);
+    if (wave_active && t + 1 < ntiles)
+      dense_tile<D>(Ks[1], Vs[1], qb, key0 + (t + 1) * 64, key1, safe_end, qpos, c, col, grp, m,
+                    lsum, oacc);
+    __syncthreads();
+    stage_store<D, KPT>(ka, va, Ks[1], Vs[1], rrow, rslot);
+    stage_load<D, KPT>(kc, vc, kh, vh, key0 + (t + 5) * 64, key1, rrow, rslot);
+    if (wave_active && t + 2 < ntiles)
+      dense_tile<D>(Ks[0], Vs[0], qb, key0 + (t + 2) * 64, key1, safe_end, qpos, c, col, grp, m,
+                    lsum, oacc);
   }
 
   if (!wave_active) return;
@@ -257,9 +319,9 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(
 
 // ---------------------------------------------------------------------------
 // Sparse draft step: grid (64-entry chunk of the key list, KV head), 1 wave.
-// The wave gathers its 64 K and V rows (16-byte loads, 16 lanes per row, so
-// each row is one contiguous 256-byte read) into LDS, all loads issued
-// before any is consumed.
+// The wave gathers its 64 K and V rows (16-byte loads, one 256-byte row per
+// 16 lanes, all issued before any is consumed) into LDS and reduces them for
+// the G query heads (G <= 16 columns of one MFMA block).
 template <int D>
 __global__ __launch_bounds__(64) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -267,11 +329,10 @@ __global__ __launch_bounds__(64) void sparse_mfma_kernel(
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, int n_entries,
     float2* __restrict__ ml, float* __restrict__ o) {
   using TM = TileMath<D>;
-  constexpr int KP = TM::KP, VP = TM::VP, DB = TM::DB;
-  constexpr int CPR = D / 8;          // chunks per row; also loads per lane
-  constexpr int KPV = 64 / (64 / CPR);  // V keys per lane (== CPR)
-  __shared__ __align__(16) uint16_t Ks[64 * KP];
-  __shared__ __align__(16) uint16_t Vt[D * VP];
+  constexpr int DB = TM::DB;
+  constexpr int CPR = D / 8;          // chunks per row == loads per lane per tensor
+  __shared__ __align__(16) uint16_t Ks[64 * D];
+  __shared__ __align__(16) uint16_t Vs[64 * D];
   __shared__ int pos_s[64];
 
   const int s = blockIdx.x, g = blockIdx.y;
@@ -283,43 +344,31 @@ __global__ __launch_bounds__(64) void sparse_mfma_kernel(
 
   KeyList kl{true, idx + (size_t)g * topk, vis_start, vis_end, topk};
   const int e = s * 64 + lane;
-  pos_s[lane] = e < n_entries ? kl.pos(e) : -1;
+  const int mypos = e < n_entries ? kl.pos(e) : -1;
+  pos_s[lane] = mypos;
   __syncthreads();
 
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
-  const int cv = lane % CPR, kg = lane / CPR;
-  uint4 kreg[CPR], vreg[KPV];
+  const int last = kl.pos(n_entries - 1);   // a valid row for the padded entries
+  uint4 kreg[CPR], vreg[CPR];
 #pragma unroll
   for (int u = 0; u < CPR; ++u) {
     const int cl = lane + 64 * u;
-    const int pk = pos_s[cl / CPR];
-    kreg[u] = pk >= 0 ? *reinterpret_cast<const uint4*>(kh + (size_t)pk * D + (cl % CPR) * 8)
-                      : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < KPV; ++u) {
-    const int pv = pos_s[KPV * kg + u];
-    vreg[u] = pv >= 0 ? *reinterpret_cast<const uint4*>(vh + (size_t)pv * D + cv * 8)
-                      : make_uint4(0, 0, 0, 0);
+    const int row = cl / CPR, slot = cl % CPR;
+    int pr = pos_s[row];
+    pr = pr >= 0 ? pr : last;
+    const size_t off = (size_t)pr * D + ((slot ^ (row % CPR)) << 3);
+    kreg[u] = *reinterpret_cast<const uint4*>(kh + off);
+    vreg[u] = *reinterpret_cast<const uint4*>(vh + off);
   }
   bf16x8_t qb[D / 32];
   load_q_operand<D>(q + (size_t)h * D, row_ok, grp, qb);
-
 #pragma unroll
   for (int u = 0; u < CPR; ++u) {
     const int cl = lane + 64 * u;
-    *reinterpret_cast<uint4*>(Ks + (cl / CPR) * KP + (cl % CPR) * 8) = kreg[u];
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int w4 = 0; w4 < KPV / 4; ++w4) {
-      uint2 w;
-      w.x = half16(vreg[4 * w4 + 0], j) | (half16(vreg[4 * w4 + 1], j) << 16);
-      w.y = half16(vreg[4 * w4 + 2], j) | (half16(vreg[4 * w4 + 3], j) << 16);
-      *reinterpret_cast<uint2*>(Vt + (cv * 8 + j) * VP + KPV * kg + 4 * w4) = w;
-    }
+    *reinterpret_cast<uint4*>(Ks + (cl / CPR) * D + ((cl % CPR) << 3)) = kreg[u];
+    *reinterpret_cast<uint4*>(Vs + (cl / CPR) * D + ((cl % CPR) << 3)) = vreg[u];
   }
   __syncthreads();
 
@@ -327,16 +376,14 @@ __global__ __launch_bounds__(64) void sparse_mfma_kernel(
   TM::scores(Ks, qb, col, grp, sacc);
   float x[16], p[16];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[kb * 4 + i] = pos_s[kb * 16 + 4 * grp + i] >= 0 ? sacc[kb][i] * c : -INFINITY;
+  for (int j = 0; j < 16; ++j)
+    x[j] = pos_s[(j >> 2) * 16 + 4 * grp + (j & 3)] >= 0 ? sacc[j >> 2][j & 3] * c : -INFINITY;
   float m = -INFINITY, lsum = 0.f;
   floatx4_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   online_update<DB>(x, p, m, lsum, oacc);
-  TM::pv(Vt, p, col, grp, oacc);
+  TM::pv(Vs, p, col, grp, oacc);
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
   if (!row_ok) return;

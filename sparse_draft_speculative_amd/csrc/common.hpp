@@ -14,6 +14,9 @@ constexpr int kWave = 64;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+// Native 16-byte vector for register staging (HIP's uint4 class is copied
+// through memory, which keeps arrays of it out of registers).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

@@ -22,13 +22,13 @@ inline int pow2_floor(long long x) {
 // = [c*kc, (c+1)*kc), one workgroup each.  kc depends only on (len,
 // n_kv_heads), never on n_q, so a query row sees the same chunks and the
 // same reduction order whatever the number of rows in the call.  kc is a
-// multiple of 64 (the tile) sized so one layer launches about 512
-// workgroups: two resident per CU on 256 CUs, i.e. a single round.
+// multiple of 192 (three 64-key tiles: the kernel's pipeline is unrolled by
+// three) sized so one layer launches about 512 workgroups: two resident per
+// CU on 256 CUs, i.e. a single round.
 inline int dense_chunk_keys(int len, int n_kv_heads) {
   const int target = n_kv_heads >= 512 ? 1 : 512 / n_kv_heads;
   int kc = (len + target - 1) / target;
-  kc = ((kc + 63) / 64) * 64;
-  if (kc < 128) kc = 128;
+  kc = ((kc + 191) / 192) * 192;
   return kc;
 }
 
