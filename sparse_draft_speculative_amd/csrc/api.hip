@@ -99,8 +99,8 @@ int sparse_splits(const std_kv_t* kv, std_vis_t vis, int topk) {
 }
 
 int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int* chunk) {
-  *chunk = dense_chunk_keys(kv->len, s->n_kv_heads);
-  return (kv->len + *chunk - 1) / *chunk;
+  *chunk = 64;                                   // tile size; splits interleave tiles
+  return dense_split_count(kv->len, s->n_kv_heads);
 }
 
 std_status_t check_ws(void* ws, size_t have, size_t need) {

@@ -2,16 +2,17 @@
 //
 //  * dense_mfma_kernel  -- the dense model's verify pass (technical summary,
 //    Methodology items 2-3: the dense model checks the gamma drafts in one
-//    pass over the full KV cache).  One workgroup streams one key chunk of
-//    one KV head ONCE for every query row of that head's GQA group (n_q*G
-//    rows, 16 per wave), so each K/V byte is read from HBM once per call.
+//    pass over the full KV cache).  One workgroup streams its share of one
+//    KV head's tiles ONCE for every query row of that head's GQA group (up
+//    to 64 of the n_q*G rows per workgroup), so each K/V byte is read from
+//    HBM once per call when n_q*G <= 64.
 //  * sparse_mfma_kernel -- the sparse model's draft step (Methodology item 2:
 //    top-K attention over the visual KV chosen at prefill).  One wave
 //    gathers 64 entries of the head's key list (prefix + selected visual
 //    positions + tail) into LDS and reduces them for the G query heads.
 //  * attn_valu_kernel   -- the same two operations on the vector ALU for
 //    fp32 caches (and any shape the MFMA kernels do not take).
-//  * combine_kernel     -- merges the per-chunk (max, sum, output) partials
+//  * combine_kernel     -- merges the per-split (max, sum, output) partials
 //    with log-sum-exp rescaling (flash-decoding style reduction pass).
 //
 // MFMA formulation (v_mfma_f32_16x16x32_bf16): scores are computed
@@ -60,14 +61,24 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, t);
 }
 
-// LDS tile of 64 K or V rows, row-major, each 16-byte chunk of row r stored
-// at chunk slot (chunk ^ (r % CPR)) so the 16 rows touched by one MFMA
-// operand read fall in distinct banks.
+// LDS tiles of 64 K or V rows, row-major, with the 16-byte chunks of each
+// row permuted (XOR swizzle) so that the reads feeding one MFMA operand hit
+// distinct banks:
+//  * K: chunk c of row r sits at slot c ^ (r % CPR).  A K-operand read takes
+//    one chunk of 16 consecutive rows.
+//  * V: chunk c of row r sits at slot c ^ 2*(r % 4).  A transpose read takes
+//    8 bytes from 4 consecutive rows x 2 chunks per 16 lanes; the XOR with
+//    2*(r % 4) spreads those over 8 distinct slots.
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static __device__ __forceinline__ int off(int row, int chunk) {   // elements
-    return row * D + ((chunk ^ (row % CPR)) << 3);
+  static __device__ __forceinline__ int slot_k(int row, int chunk) { return chunk ^ (row % CPR); }
+  static __device__ __forceinline__ int slot_v(int row, int chunk) { return chunk ^ ((row & 3) << 1); }
+  static __device__ __forceinline__ int off_k(int row, int chunk) {   // elements
+    return row * D + (slot_k(row, chunk) << 3);
+  }
+  static __device__ __forceinline__ int off_v(int row, int chunk) {
+    return row * D + (slot_v(row, chunk) << 3);
   }
 };
 
@@ -87,7 +98,7 @@ struct TileMath {
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         const uint4 a = *reinterpret_cast<const uint4*>(
-            Ks + Tile<D>::off(kb * 16 + col, KST * grp + kk));
+            Ks + Tile<D>::off_k(kb * 16 + col, KST * grp + kk));
         acc = mfma_bf16(as_bf16x8(a), qb[kk], acc);
       }
       sacc[kb] = acc;
@@ -115,8 +126,8 @@ struct TileMath {
       for (int db = 0; db < DB; ++db) {
         const int chunk = 2 * db + (rc >> 1);
         const int e = 4 * (rc & 1);
-        const uint2 lo = lds_read_tr16(Vs + Tile<D>::off(row0, chunk) + e);
-        const uint2 hi = lds_read_tr16(Vs + Tile<D>::off(row0 + 16, chunk) + e);
+        const uint2 lo = lds_read_tr16(Vs + Tile<D>::off_v(row0, chunk) + e);
+        const uint2 hi = lds_read_tr16(Vs + Tile<D>::off_v(row0 + 16, chunk) + e);
         oacc[db] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, oacc[db]);
       }
     }
@@ -167,19 +178,19 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, bool ok, in
 }
 
 // Move one 64-row tile of K and V: global -> registers (rows clamped to
-// the last valid one) and registers -> LDS (swizzled chunk slots).
+// the last valid one, key1 - 1, so every load is in bounds and the data past
+// the end is finite; it is masked out of the softmax) and registers -> LDS
+// (swizzled chunk slots).
 template <int D, int KPT>
 __device__ __forceinline__ void stage_load(u32x4_t (&kr)[KPT], u32x4_t (&vr)[KPT],
                                            const uint16_t* kh, const uint16_t* vh, int t0,
                                            int key1, const int (&rrow)[KPT],
                                            const int (&rslot)[KPT]) {
-  constexpr int CPR = D / 8;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int key = min(t0 + rrow[u], key1 - 1);
-    const size_t off = (size_t)key * D + ((rslot[u] ^ (rrow[u] % CPR)) << 3);
-    kr[u] = *reinterpret_cast<const u32x4_t*>(kh + off);
-    vr[u] = *reinterpret_cast<const u32x4_t*>(vh + off);
+    const size_t base = (size_t)min(t0 + rrow[u], key1 - 1) * D;
+    kr[u] = *reinterpret_cast<const u32x4_t*>(kh + base + (Tile<D>::slot_k(rrow[u], rslot[u]) << 3));
+    vr[u] = *reinterpret_cast<const u32x4_t*>(vh + base + (Tile<D>::slot_v(rrow[u], rslot[u]) << 3));
   }
 }
 
@@ -194,71 +205,176 @@ __device__ __forceinline__ void stage_store(const u32x4_t (&kr)[KPT], const u32x
   }
 }
 
-// ---------------------------------------------------------------------------
-// Dense verify: grid (key chunk, KV head, 64-row block), 256 threads.
-//
-// Pipeline per 64-key tile t (one barrier per tile): tile t+1 is written
-// from registers into the other LDS buffer while tile t is reduced, and the
-// loads of tiles t+2 and t+3 are in flight in two more register buffers.
-// Loads are branch-free: rows past the chunk end are clamped to the last
-// valid row (finite data, masked out of the softmax).
-// Reduce one 64-key tile of LDS buffer ``buf`` into the wave's softmax state.
-template <int D>
-__device__ __forceinline__ void dense_tile(const uint16_t* Ks, const uint16_t* Vs,
-                                           const bf16x8_t* qb, int t0, int key1, int safe_end,
-                                           int qpos, float c, int col, int grp, float& m,
-                                           float& lsum, floatx4_t* oacc) {
-  using TM = TileMath<D>;
-  floatx4_t sacc[4];
-  TM::scores(Ks, qb, col, grp, sacc);
-  float x[16], p[16];
-  if (t0 + 64 <= safe_end) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = sacc[j >> 2][j & 3] * c;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = t0 + (j >> 2) * 16 + 4 * grp + (j & 3);
-      x[j] = (key < key1 && key <= qpos) ? sacc[j >> 2][j & 3] * c : -INFINITY;
-    }
-  }
-  online_update<TM::DB>(x, p, m, lsum, oacc);
-  TM::pv(Vs, p, col, grp, oacc);
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 cross-row permutes, no LDS round trip.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Dense verify, one wave's share of a 64-key tile: the 32 keys of key half
+// kh (key blocks 2kh, 2kh+1) against the wave's two 16-column query blocks.
+// Half the keys per wave halves the LDS operand traffic compared with every
+// wave reading the whole tile.
 template <int D>
-__global__ __launch_bounds__(256) void dense_mfma_kernel(
+struct HalfTile {
+  static constexpr int KST = D / 32;
+  static constexpr int DB = D / 16;
+
+  static __device__ __forceinline__ void run(const uint16_t* Ks, const uint16_t* Vs,
+                                             const bf16x8_t (*qb)[D / 32], int nblocks, int kh,
+                                             int t0, int len, int safe_end, const int* qpos,
+                                             float c, int col, int grp, float* m, float* lsum,
+                                             floatx4_t (*oacc)[D / 16]) {
+    // S^T for the two key blocks and the active query blocks
+    floatx4_t sacc[2][2];
+#pragma unroll
+    for (int kbi = 0; kbi < 2; ++kbi) {
+      const int row = (2 * kh + kbi) * 16 + col;
+      uint4 a[KST];
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk)
+        a[kk] = *reinterpret_cast<const uint4*>(Ks + Tile<D>::off_k(row, KST * grp + kk));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (nb < nblocks) {
+#pragma unroll
+          for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kk]), qb[nb][kk], acc);
+        }
+        sacc[kbi][nb] = acc;
+      }
+    }
+    float p[2][8];
+    const bool interior = t0 + 64 <= safe_end;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if (nb >= nblocks) break;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float sv = sacc[j >> 2][nb][j & 3] * c;
+        if (interior) {
+          x[j] = sv;
+        } else {
+          const int key = t0 + (2 * kh + (j >> 2)) * 16 + 4 * grp + (j & 3);
+          x[j] = (key < len && key <= qpos[nb]) ? sv : -INFINITY;
+        }
+      }
+      float tmax = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
+      tmax = max_over_groups(tmax);
+      if (tmax > m[nb] + kLazyMax) {     // rare: see online_update
+        const float alpha = fast_exp2(m[nb] - tmax);
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[nb][db] *= alpha;
+        m[nb] = tmax;
+      }
+      const float msafe = (m[nb] == -INFINITY) ? 0.f : m[nb];
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[nb][j] = fast_exp2(x[j] - msafe);
+        ps += p[nb][j];
+      }
+      lsum[nb] += ps;
+    }
+    // O^T += V^T P^T over the 32 keys (one MFMA step); the V^T operand is
+    // shared by both query blocks.
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uint4 pw;
+      pw.x = pack_bf16x2(p[nb][0], p[nb][1]);
+      pw.y = pack_bf16x2(p[nb][2], p[nb][3]);
+      pw.z = pack_bf16x2(p[nb][4], p[nb][5]);
+      pw.w = pack_bf16x2(p[nb][6], p[nb][7]);
+      pb[nb] = as_bf16x8(pw);
+    }
+    const int r4 = col >> 2, rc = col & 3;
+    const int row0 = 32 * kh + 4 * grp + r4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 2 * db + (rc >> 1);
+      const int e = 4 * (rc & 1);
+      const uint2 lo = lds_read_tr16(Vs + Tile<D>::off_v(row0, chunk) + e);
+      const uint2 hi = lds_read_tr16(Vs + Tile<D>::off_v(row0 + 16, chunk) + e);
+      const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        if (nb < nblocks) oacc[nb][db] = mfma_bf16(va, pb[nb], oacc[nb][db]);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Dense verify: grid (split, KV head, 64-row block), 256 threads.
+//
+// The len keys form ceil(len/64) tiles of 64; split s takes tiles s,
+// s + S, s + 2S, ... (S splits, a function of len and H_kv only), so at any
+// moment the workgroups of a head sweep one contiguous region of the cache.
+// Waves: wave w reduces key half (w & 1) of every tile for query columns
+// 32*(w >> 1) .. +31 of the row block; the two key halves are merged in LDS
+// at the end.
+//
+// Pipeline per tile (one barrier per tile): tile i+1 moves from registers
+// into the other LDS buffer while tile i is reduced.  Loads and stores are
+// unconditional (indices past the end re-read the last row), so the number
+// of loads in flight is the same on every path and the compiler waits only
+// for the buffer it is about to store.
+template <int D>
+__global__ __launch_bounds__(256, 2) void dense_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, int len, int n_q, float c,
-    int chunk, float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
+    int splits, float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
   constexpr int DB = D / 16;
   constexpr int CPR = D / 8;
   constexpr int KPT = 64 * CPR / 256;   // 16-byte chunks per thread per tensor
-  __shared__ __align__(16) uint16_t Ks[2][64 * D];
-  __shared__ __align__(16) uint16_t Vs[2][64 * D];
+  constexpr int TILE = 64 * D;          // elements of one K or V tile
+  __shared__ __align__(16) uint16_t smem[4 * TILE];   // K[2], V[2]; reused for the merge
+  uint16_t* Ks0 = smem;
+  uint16_t* Ks1 = smem + TILE;
+  uint16_t* Vs0 = smem + 2 * TILE;
+  uint16_t* Vs1 = smem + 3 * TILE;
 
   const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kh = wave & 1, qh = wave >> 1;
   const int G = hq / hkv;
   const int Rg = n_q * G;
   const int col = lane & 15, grp = lane >> 4;
-  const int rho = rb * 64 + wave * 16 + col;
-  const bool row_ok = rho < Rg;
-  const int qi = row_ok ? rho / G : 0;
-  const int h = g * G + (row_ok ? rho % G : 0);
-  const int qpos = len - n_q + qi;
-  const bool wave_active = rb * 64 + wave * 16 < Rg;
+  const int cbase = rb * 64 + qh * 32;                 // first query row of this wave
+  const int nblocks = Rg - cbase <= 0 ? 0 : (Rg - cbase > 16 ? 2 : 1);
+  int qi[2], hh[2], qpos[2];
+  bool rok[2];
+  bf16x8_t qb[2][D / 32];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int rho = cbase + nb * 16 + col;
+    rok[nb] = rho < Rg;
+    qi[nb] = rok[nb] ? rho / G : 0;
+    hh[nb] = g * G + (rok[nb] ? rho % G : 0);
+    qpos[nb] = len - n_q + qi[nb];
+    load_q_operand<D>(q + ((size_t)qi[nb] * hq + hh[nb]) * D, rok[nb], grp, qb[nb]);
+  }
 
-  bf16x8_t qb[D / 32];
-  load_q_operand<D>(q + ((size_t)qi * hq + h) * D, row_ok, grp, qb);
+  const int ntiles_all = (len + 63) / 64;
+  const int ntiles = (ntiles_all - s + splits - 1) / splits;   // tiles of this split
+  const int safe_end = len - n_q + 1;    // keys < safe_end: visible to every row
+  const uint16_t* kh_ = k + (size_t)g * capacity * D;
+  const uint16_t* vh_ = v + (size_t)g * capacity * D;
+  auto tile_key = [&](int i) { return (s + i * splits) * 64; };
 
-  const int key0 = s * chunk;
-  const int key1 = min(len, key0 + chunk);
-  const int safe_end = min(key1, len - n_q + 1);   // keys < safe_end: visible to every row
-  const uint16_t* kh = k + (size_t)g * capacity * D;
-  const uint16_t* vh = v + (size_t)g * capacity * D;
-
-  // thread -> (row, slot) of each chunk it moves; global chunk = slot ^ (row % CPR)
   int rrow[KPT], rslot[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
@@ -267,54 +383,75 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(
     rslot[u] = cl % CPR;
   }
 
-  float m = -INFINITY, lsum = 0.f;
-  floatx4_t oacc[DB];
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  floatx4_t oacc[2][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[nb][db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Pipeline per 64-key tile t (one barrier per tile): tile t+1 moves from
-  // registers into the other LDS buffer while tile t is reduced, and tiles
-  // t+2, t+3 are in flight from HBM in two more register buffers.  Loads
-  // and stores are unconditional (tiles past the chunk re-read its last
-  // row), so the number of loads in flight is the same on every path and
-  // the compiler waits only for the buffer it is about to store.  The loop
-  // is unrolled by three so the three register buffers stay static.
-  const int ntiles = (key1 - key0 + 63) / 64;
-  u32x4_t ka[KPT], va[KPT], kb_[KPT], vb[KPT], kc[KPT], vc[KPT];
-  stage_load<D, KPT>(ka, va, kh, vh, key0, key1, rrow, rslot);
-  stage_load<D, KPT>(kb_, vb, kh, vh, key0 + 64, key1, rrow, rslot);
-  stage_load<D, KPT>(kc, vc, kh, vh, key0 + 128, key1, rrow, rslot);
-  stage_store<D, KPT>(ka, va, Ks[0], Vs[0], rrow, rslot);
-  for (int t = 0; t < ntiles; t += 3) {
+  // Two register buffers: a buffer is refilled right after its contents
+  // are written to LDS, so tiles i+2 and i+3 are in flight while tile i is
+  // reduced.  Unrolled by two so the buffers stay static.
+  u32x4_t ka[KPT], va[KPT], kb_[KPT], vb[KPT];
+  stage_load<D, KPT>(ka, va, kh_, vh_, tile_key(0), len, rrow, rslot);
+  stage_store<D, KPT>(ka, va, Ks0, Vs0, rrow, rslot);
+  stage_load<D, KPT>(ka, va, kh_, vh_, tile_key(1), len, rrow, rslot);
+  stage_load<D, KPT>(kb_, vb, kh_, vh_, tile_key(2), len, rrow, rslot);
+  for (int i = 0; i < ntiles; i += 2) {
     __syncthreads();
-    stage_store<D, KPT>(kb_, vb, Ks[1], Vs[1], rrow, rslot);
-    stage_load<D, KPT>(ka, va, kh, vh, key0 + (t + 3) * 64, key1, rrow, rslot);
-    if (wave_active)
-      dense_tile<D>(Ks[0], Vs[0], qb, key0 + t * 64, key1, safe_end, qpos, c, col, grp, m, lsum,
-                    oacc);
+    stage_store<D, KPT>(ka, va, Ks1, Vs1, rrow, rslot);
+    stage_load<D, KPT>(ka, va, kh_, vh_, tile_key(i + 3), len, rrow, rslot);
+    if (nblocks)
+      HalfTile<D>::run(Ks0, Vs0, qb, nblocks, kh, tile_key(i), len, safe_end, qpos, c, col, grp,
+                       m, lsum, oacc);
     __syncthreads();
-    stage_store<D, KPT>(kc, vc, Ks[0], Vs[0], rrow, rslot);
-    stage_load<D, KPT>(kb_, vb, kh, vh, key0 + (t + 4) * 64, key1, rrow, rslot);
-    if (wave_active && t + 1 < ntiles)
-      dense_tile<D>(Ks[1], Vs[1], qb, key0 + (t + 1) * 64, key1, safe_end, qpos, c, col, grp, m,
-                    lsum, oacc);
-    __syncthreads();
-    stage_store<D, KPT>(ka, va, Ks[1], Vs[1], rrow, rslot);
-    stage_load<D, KPT>(kc, vc, kh, vh, key0 + (t + 5) * 64, key1, rrow, rslot);
-    if (wave_active && t + 2 < ntiles)
-      dense_tile<D>(Ks[0], Vs[0], qb, key0 + (t + 2) * 64, key1, safe_end, qpos, c, col, grp, m,
-                    lsum, oacc);
+    stage_store<D, KPT>(kb_, vb, Ks0, Vs0, rrow, rslot);
+    stage_load<D, KPT>(kb_, vb, kh_, vh_, tile_key(i + 4), len, rrow, rslot);
+    if (nblocks && i + 1 < ntiles)
+      HalfTile<D>::run(Ks1, Vs1, qb, nblocks, kh, tile_key(i + 1), len, safe_end, qpos, c, col,
+                       grp, m, lsum, oacc);
   }
 
-  if (!wave_active) return;
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  if (!row_ok) return;
-  const size_t slot = (size_t)s * rows_total + (size_t)qi * hq + h;
-  if (grp == 0) ml[slot] = make_float2(m, lsum);
+  // merge the two key halves: odd waves hand (m, l, O) to their even partner
+  constexpr int XS = 2 * (2 + 4 * DB);                 // floats per lane
+  float* xch = reinterpret_cast<float*>(smem);
+  __syncthreads();
+  if (kh == 1 && nblocks) {
+    float* dst = xch + (size_t)(qh * 64 + lane) * XS;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    *reinterpret_cast<floatx4_t*>(o + slot * D + db * 16 + 4 * grp) = oacc[db];
+    for (int nb = 0; nb < 2; ++nb) {
+      dst[nb * (2 + 4 * DB) + 0] = m[nb];
+      dst[nb * (2 + 4 * DB) + 1] = lsum[nb];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[nb * (2 + 4 * DB) + 2 + 4 * db + i] = oacc[nb][db][i];
+    }
+  }
+  __syncthreads();
+  if (kh == 1 || !nblocks) return;
+  const float* src = xch + (size_t)(qh * 64 + lane) * XS;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    if (nb >= nblocks) break;
+    const float m1 = src[nb * (2 + 4 * DB) + 0];
+    const float l1 = src[nb * (2 + 4 * DB) + 1];
+    const float M = fmaxf(m[nb], m1);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    const float a0 = fast_exp2(m[nb] - Ms), a1 = fast_exp2(m1 - Ms);
+    const float L = sum_over_groups(lsum[nb] * a0 + l1 * a1);
+    if (!rok[nb]) continue;
+    const size_t slot = (size_t)s * rows_total + (size_t)qi[nb] * hq + hh[nb];
+    if (grp == 0) ml[slot] = make_float2(M, L);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      floatx4_t r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = oacc[nb][db][i] * a0 + src[nb * (2 + 4 * DB) + 2 + 4 * db + i] * a1;
+      *reinterpret_cast<floatx4_t*>(o + slot * D + db * 16 + 4 * grp) = r;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -351,24 +488,24 @@ __global__ __launch_bounds__(64) void sparse_mfma_kernel(
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
   const int last = kl.pos(n_entries - 1);   // a valid row for the padded entries
-  uint4 kreg[CPR], vreg[CPR];
+  u32x4_t kreg[CPR], vreg[CPR];
 #pragma unroll
   for (int u = 0; u < CPR; ++u) {
     const int cl = lane + 64 * u;
     const int row = cl / CPR, slot = cl % CPR;
     int pr = pos_s[row];
     pr = pr >= 0 ? pr : last;
-    const size_t off = (size_t)pr * D + ((slot ^ (row % CPR)) << 3);
-    kreg[u] = *reinterpret_cast<const uint4*>(kh + off);
-    vreg[u] = *reinterpret_cast<const uint4*>(vh + off);
+    const size_t base = (size_t)pr * D;
+    kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base + (Tile<D>::slot_k(row, slot) << 3));
+    vreg[u] = *reinterpret_cast<const u32x4_t*>(vh + base + (Tile<D>::slot_v(row, slot) << 3));
   }
   bf16x8_t qb[D / 32];
   load_q_operand<D>(q + (size_t)h * D, row_ok, grp, qb);
 #pragma unroll
   for (int u = 0; u < CPR; ++u) {
     const int cl = lane + 64 * u;
-    *reinterpret_cast<uint4*>(Ks + (cl / CPR) * D + ((cl % CPR) << 3)) = kreg[u];
-    *reinterpret_cast<uint4*>(Vs + (cl / CPR) * D + ((cl % CPR) << 3)) = vreg[u];
+    *reinterpret_cast<u32x4_t*>(Ks + (cl / CPR) * D + ((cl % CPR) << 3)) = kreg[u];
+    *reinterpret_cast<u32x4_t*>(Vs + (cl / CPR) * D + ((cl % CPR) << 3)) = vreg[u];
   }
   __syncthreads();
 
@@ -557,7 +694,8 @@ hipError_t launch_valu(const AttnArgs& a, const KeyList& kl, int n_entries, hipS
   dim3 grid(rows_group, a.hkv, a.splits);
   attn_valu_kernel<T, D><<<grid, 64, 0, st>>>(
       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-      a.hq, a.hkv, a.capacity, a.len, a.n_q, a.scale * kLog2e, kl, n_entries, a.chunk,
+      a.hq, a.hkv, a.capacity, a.len, a.n_q, a.scale * kLog2e, kl, n_entries,
+      a.sparse ? a.chunk : (n_entries + a.splits - 1) / a.splits,
       reinterpret_cast<float2*>(a.ml), a.o, a.n_q * a.hq);
   return hipGetLastError();
 }
@@ -577,7 +715,7 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
     const int rows_group = a.n_q * (a.hq / a.hkv);
     dim3 grid(a.splits, a.hkv, (rows_group + 63) / 64);
     dense_mfma_kernel<D><<<grid, 256, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, a.len, a.n_q,
-                                               c, a.chunk, reinterpret_cast<float2*>(a.ml), a.o,
+                                               c, a.splits, reinterpret_cast<float2*>(a.ml), a.o,
                                                a.n_q * a.hq);
   }
   return hipGetLastError();

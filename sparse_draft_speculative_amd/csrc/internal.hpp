@@ -18,18 +18,15 @@ inline int pow2_floor(long long x) {
 // ---------------------------------------------------------------------------
 // Split-K geometry.
 //
-// Dense verify: keys [0, len) are cut into chunks of kc positions, chunk c
-// = [c*kc, (c+1)*kc), one workgroup each.  kc depends only on (len,
-// n_kv_heads), never on n_q, so a query row sees the same chunks and the
-// same reduction order whatever the number of rows in the call.  kc is a
-// multiple of 192 (three 64-key tiles: the kernel's pipeline is unrolled by
-// three) sized so one layer launches about 512 workgroups: two resident per
-// CU on 256 CUs, i.e. a single round.
-inline int dense_chunk_keys(int len, int n_kv_heads) {
+// Dense verify: the len keys form ceil(len/64) tiles of 64 keys; split s of
+// S takes tiles s, s+S, s+2S, ...  S depends only on (len, n_kv_heads),
+// never on n_q, so a query row sees the same splits and the same reduction
+// order whatever the number of rows in the call.  S is sized so one layer
+// launches about 512 workgroups: two resident per CU on 256 CUs, one round.
+inline int dense_split_count(int len, int n_kv_heads) {
+  const int tiles = (len + 63) / 64;
   const int target = n_kv_heads >= 512 ? 1 : 512 / n_kv_heads;
-  int kc = (len + target - 1) / target;
-  kc = ((kc + 191) / 192) * 192;
-  return kc;
+  return tiles < target ? tiles : target;
 }
 
 // Sparse decode: the per-head key list (prefix + selected + tail) is cut
