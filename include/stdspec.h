@@ -37,7 +37,8 @@
  * - Workspace: each call that needs scratch takes a caller-allocated device
  *   buffer of at least the size its *_workspace query returns (256-byte
  *   aligned).  Its contents need no initialisation and are garbage after
- *   the call.  Two calls in flight at once need two workspaces.
+ *   the call.  A workspace serves one call at a time: two calls in flight at
+ *   once (on different streams) need two workspaces.
  */
 #ifndef STDSPEC_H
 #define STDSPEC_H

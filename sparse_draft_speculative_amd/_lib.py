@@ -133,8 +133,9 @@ def kv_desc(k, v, length):
 
 
 def _workspace(nbytes, device, workspace):
+    # zero-filled: the library's ticket counters must start at zero
     if workspace is None:
-        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     _dev(workspace, "workspace")
     return workspace
 

@@ -455,34 +455,42 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Sparse draft step: grid (64-entry chunk of the key list, KV head), 1 wave.
-// The wave gathers its 64 K and V rows (16-byte loads, one 256-byte row per
-// 16 lanes, all issued before any is consumed) into LDS and reduces them for
-// the G query heads (G <= 16 columns of one MFMA block).
+// Sparse draft step: grid (split of 256 key-list entries, KV head), 4 waves.
+//
+// Each wave gathers one 64-entry tile of the head's key list (prefix +
+// selected visual positions + tail) into its own LDS region -- one
+// contiguous 256-byte row per 16 lanes, all loads issued before any is used
+// -- and reduces it for the G <= 16 query heads of the group (one MFMA
+// column block).  The four waves merge in LDS and the workgroup writes one
+// (max, sum, output) partial for the combine pass.
+constexpr int kSparseWaves = 4;
+
 template <int D>
-__global__ __launch_bounds__(64) void sparse_mfma_kernel(
+__global__ __launch_bounds__(256) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, int n_entries,
-    float2* __restrict__ ml, float* __restrict__ o) {
+    int splits, float2* __restrict__ ml, float* __restrict__ o) {
   using TM = TileMath<D>;
   constexpr int DB = TM::DB;
   constexpr int CPR = D / 8;          // chunks per row == loads per lane per tensor
-  __shared__ __align__(16) uint16_t Ks[64 * D];
-  __shared__ __align__(16) uint16_t Vs[64 * D];
-  __shared__ int pos_s[64];
+  constexpr int TILE = 64 * D;
+  __shared__ __align__(16) uint16_t smem[kSparseWaves * 2 * TILE];
+  __shared__ int pos_s[kSparseWaves * 64];
 
   const int s = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = hq / hkv;
   const int col = lane & 15, grp = lane >> 4;
   const bool row_ok = col < G;
   const int h = g * G + (row_ok ? col : 0);
+  uint16_t* Ks = smem + wave * 2 * TILE;
+  uint16_t* Vs = Ks + TILE;
+  int* pw = pos_s + wave * 64;
 
   KeyList kl{true, idx + (size_t)g * topk, vis_start, vis_end, topk};
-  const int e = s * 64 + lane;
-  const int mypos = e < n_entries ? kl.pos(e) : -1;
-  pos_s[lane] = mypos;
+  const int e = s * (64 * kSparseWaves) + wave * 64 + lane;
+  pw[lane] = e < n_entries ? kl.pos(e) : -1;
   __syncthreads();
 
   const uint16_t* kh = k + (size_t)g * capacity * D;
@@ -493,7 +501,7 @@ __global__ __launch_bounds__(64) void sparse_mfma_kernel(
   for (int u = 0; u < CPR; ++u) {
     const int cl = lane + 64 * u;
     const int row = cl / CPR, slot = cl % CPR;
-    int pr = pos_s[row];
+    int pr = pw[row];
     pr = pr >= 0 ? pr : last;
     const size_t base = (size_t)pr * D;
     kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base + (Tile<D>::slot_k(row, slot) << 3));
@@ -507,28 +515,71 @@ __global__ __launch_bounds__(64) void sparse_mfma_kernel(
     *reinterpret_cast<u32x4_t*>(Ks + (cl / CPR) * D + ((cl % CPR) << 3)) = kreg[u];
     *reinterpret_cast<u32x4_t*>(Vs + (cl / CPR) * D + ((cl % CPR) << 3)) = vreg[u];
   }
-  __syncthreads();
+  // the wave reads back only its own region: no workgroup barrier needed
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS stores done
+  __builtin_amdgcn_wave_barrier();
 
-  floatx4_t sacc[4];
-  TM::scores(Ks, qb, col, grp, sacc);
-  float x[16], p[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    x[j] = pos_s[(j >> 2) * 16 + 4 * grp + (j & 3)] >= 0 ? sacc[j >> 2][j & 3] * c : -INFINITY;
   float m = -INFINITY, lsum = 0.f;
   floatx4_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  online_update<DB>(x, p, m, lsum, oacc);
-  TM::pv(Vs, p, col, grp, oacc);
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  if (!row_ok) return;
-  const size_t slot = (size_t)s * hq + h;
-  if (grp == 0) ml[slot] = make_float2(m, lsum);
+  if (s * (64 * kSparseWaves) + wave * 64 < n_entries) {
+    floatx4_t sacc[4];
+    TM::scores(Ks, qb, col, grp, sacc);
+    float x[16], p[16];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    *reinterpret_cast<floatx4_t*>(o + slot * D + db * 16 + 4 * grp) = oacc[db];
+    for (int j = 0; j < 16; ++j)
+      x[j] = pw[(j >> 2) * 16 + 4 * grp + (j & 3)] >= 0 ? sacc[j >> 2][j & 3] * c : -INFINITY;
+    online_update<DB>(x, p, m, lsum, oacc);
+    TM::pv(Vs, p, col, grp, oacc);
+  }
+  lsum = sum_over_groups(lsum);
+
+  // merge the four waves: each lane's (m, l, 4*DB outputs) through LDS
+  constexpr int XS = 2 + 4 * DB;
+  float* xch = reinterpret_cast<float*>(smem);
+  __syncthreads();                     // every wave is done with its tile
+  {
+    float* dst = xch + (size_t)(wave * 64 + lane) * XS;
+    dst[0] = m;
+    dst[1] = lsum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[2 + 4 * db + i] = oacc[db][i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float mw[kSparseWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSparseWaves; ++w) {
+      mw[w] = xch[(size_t)(w * 64 + lane) * XS];
+      M = fmaxf(M, mw[w]);
+    }
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+    floatx4_t acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kSparseWaves; ++w) {
+      const float* src = xch + (size_t)(w * 64 + lane) * XS;
+      const float a = fast_exp2(mw[w] - Ms);
+      L = fmaf(src[1], a, L);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[db][i] = fmaf(src[2 + 4 * db + i], a, acc[db][i]);
+    }
+    if (row_ok) {
+      const size_t slot = (size_t)s * hq + h;
+      if (grp == 0) ml[slot] = make_float2(M, L);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<floatx4_t*>(o + slot * D + db * 16 + 4 * grp) = acc[db];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -601,12 +652,12 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 
 // ---------------------------------------------------------------------------
 // Split combine: out[r] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
-// M = max_s m_s.  One 256-thread workgroup per query row; the splits are
-// spread over the threads (weights staged in LDS), each thread then sums a
-// float4 column over a strided subset of splits and the subsets are added
-// in a fixed order, so the result does not depend on timing.
+// M = max_s m_s.  One 256-thread workgroup per query row.  Thread (sg, dq)
+// merges splits sg, sg + NSG, ... online (running max, rescale on a new
+// max), reading each split's (m, l) together with its float4 of outputs in
+// the same round of loads; the NSG groups are then merged in LDS in a fixed
+// order, so the result does not depend on timing.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineMaxSplits = 4096;   // LDS weights; larger S loops in chunks
 
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
@@ -614,65 +665,52 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     T* __restrict__ out) {
   constexpr int DQ = D / 4;                      // float4 columns
   constexpr int NSG = kCombineThreads / DQ;      // split groups
-  __shared__ float wsh[kCombineMaxSplits];
-  __shared__ float red[kCombineThreads / kWave];
   __shared__ float4 part[NSG][DQ];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  float M = -INFINITY;
-  for (int s = tid; s < splits; s += kCombineThreads) M = fmaxf(M, ml[(size_t)s * rows + r].x);
-  M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < kCombineThreads / kWave; ++w) M = fmaxf(M, red[w]);
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-  __syncthreads();
-
+  __shared__ float2 stat[NSG][DQ];
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int dq = tid % DQ, sg = tid / DQ;
-  float Lloc = 0.f;
+  float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < splits; s0 += kCombineMaxSplits) {
-    const int s1 = min(splits, s0 + kCombineMaxSplits);
-    for (int s = s0 + tid; s < s1; s += kCombineThreads) {
-      const float2 st = ml[(size_t)s * rows + r];
-      const float w = fast_exp2(st.x - Ms);
-      wsh[s - s0] = w;
-      Lloc = fmaf(st.y, w, Lloc);
-    }
-    __syncthreads();
 #pragma unroll 4
-    for (int s = s0 + sg; s < s1; s += NSG) {
-      const float w = wsh[s - s0];
-      const float4 x = *reinterpret_cast<const float4*>(o + ((size_t)s * rows + r) * D + 4 * dq);
-      acc.x = fmaf(w, x.x, acc.x);
-      acc.y = fmaf(w, x.y, acc.y);
-      acc.z = fmaf(w, x.z, acc.z);
-      acc.w = fmaf(w, x.w, acc.w);
-    }
-    __syncthreads();
+  for (int s = sg; s < splits; s += NSG) {
+    const float2 st = ml[(size_t)s * rows + r];
+    const float4 x = *reinterpret_cast<const float4*>(o + ((size_t)s * rows + r) * D + 4 * dq);
+    const float Mn = fmaxf(M, st.x);
+    const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+    const float a = fast_exp2(M - Ms), b = fast_exp2(st.x - Ms);
+    L = L * a + st.y * b;
+    acc.x = acc.x * a + x.x * b;
+    acc.y = acc.y * a + x.y * b;
+    acc.z = acc.z * a + x.z * b;
+    acc.w = acc.w * a + x.w * b;
+    M = Mn;
   }
-  Lloc = wave_sum(Lloc);
-  if (lane == 0) red[wave] = Lloc;
   part[sg][dq] = acc;
+  stat[sg][dq] = make_float2(M, L);
   __syncthreads();
   if (tid < DQ) {
-    float L = 0.f;
+    float Mt = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kCombineThreads / kWave; ++w) L += red[w];
-    float4 a = part[0][tid];
+    for (int g = 0; g < NSG; ++g) Mt = fmaxf(Mt, stat[g][tid].x);
+    const float Ms = (Mt == -INFINITY) ? 0.f : Mt;
+    float Lt = 0.f;
+    float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int g = 1; g < NSG; ++g) {
+    for (int g = 0; g < NSG; ++g) {
+      const float w = fast_exp2(stat[g][tid].x - Ms);
+      Lt = fmaf(stat[g][tid].y, w, Lt);
       const float4 b = part[g][tid];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      a4.x = fmaf(b.x, w, a4.x);
+      a4.y = fmaf(b.y, w, a4.y);
+      a4.z = fmaf(b.z, w, a4.z);
+      a4.w = fmaf(b.w, w, a4.w);
     }
-    const float inv = 1.f / L;
+    const float inv = 1.f / Lt;
     const size_t base = (size_t)r * D + 4 * tid;
-    Elem<T>::store(out, base + 0, a.x * inv);
-    Elem<T>::store(out, base + 1, a.y * inv);
-    Elem<T>::store(out, base + 2, a.z * inv);
-    Elem<T>::store(out, base + 3, a.w * inv);
+    Elem<T>::store(out, base + 0, a4.x * inv);
+    Elem<T>::store(out, base + 1, a4.y * inv);
+    Elem<T>::store(out, base + 2, a4.z * inv);
+    Elem<T>::store(out, base + 3, a4.w * inv);
   }
 }
 
@@ -708,9 +746,9 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   if (a.sparse) {
     const int n_entries = sparse_list_len(a.len, a.vis_start, a.vis_len, a.topk);
-    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv), 64, 0, st>>>(
+    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv), 256, 0, st>>>(
         q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
-        a.topk, n_entries, reinterpret_cast<float2*>(a.ml), a.o);
+        a.topk, n_entries, a.splits, reinterpret_cast<float2*>(a.ml), a.o);
   } else {
     const int rows_group = a.n_q * (a.hq / a.hkv);
     dim3 grid(a.splits, a.hkv, (rows_group + 63) / 64);

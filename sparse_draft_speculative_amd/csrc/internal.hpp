@@ -30,15 +30,17 @@ inline int dense_split_count(int len, int n_kv_heads) {
 }
 
 // Sparse decode: the per-head key list (prefix + selected + tail) is cut
-// into chunks of 64 entries, one wave each.
-constexpr int kSparseChunk = 64;
+// into splits of 256 entries (four 64-entry tiles, one wave each).
+constexpr int kSparseChunk = 256;
 
 inline int sparse_list_len(int len, int vis_start, int vis_len, int topk) {
   return vis_start + topk + (len - (vis_start + vis_len));
 }
 
+// Split-K workspace: [ml: splits x rows x float2][o: splits x rows x
+// head_dim floats]; scratch, no initialisation needed.
 struct SplitWorkspace {
-  int splits;     // number of key chunks
+  int splits;     // number of key splits
   int rows;       // query rows = n_q * n_q_heads
   int head_dim;
   size_t ml_bytes, o_bytes;

@@ -283,3 +283,28 @@ def test_accept_matches_oracle(lib, gamma, vocab, dtype, agree, ties):
         assert int(n_out.item()) == ref_n
         assert int(seq.item()) == 1000 + ref_n
         assert np.allclose(margins.cpu().numpy(), ref_m, rtol=1e-6, atol=1e-6)
+
+
+def test_sparse_decode_reuses_one_workspace(lib):
+    """Back-to-back calls of different sizes sharing one (dirty) workspace
+    stay correct: the workspace is scratch and needs no initialisation."""
+    cfg = synth.config("c2")
+    lay = layer(cfg)
+    idx_ref, _ = oracle_idx(cfg, lay)
+    idx = torch.from_numpy(idx_ref.astype(np.int32)).cuda()
+    shape = lib.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+    nbytes = lib.std_sparse_decode_workspace(shape, lay["k"], cfg.capacity, cfg.vis_start,
+                                             cfg.vis_len, cfg.topk)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")   # garbage
+    kf, vf = f64(lay["k"]), f64(lay["v"])
+    for rep in range(3):
+        for j in (cfg.gamma - 1, 0, 2):
+            length = cfg.draft_len(j)
+            sub = idx[:, : cfg.topk - 100 * rep].contiguous()   # shrinking key sets
+            q = lay["q_draft"][j].contiguous()
+            out = lib.std_sparse_decode_attn(q, lay["k"], lay["v"], length, cfg.vis_start,
+                                             cfg.vis_len, sub, workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.sparse_decode(f64(q), kf, vf, length, cfg.vis_start, cfg.vis_len,
+                                       idx_ref[:, : cfg.topk - 100 * rep])
+            assert max_abs(f64(out), ref) <= TOL[cfg.dtype]
