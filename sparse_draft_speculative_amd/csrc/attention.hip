@@ -29,6 +29,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "tile.hpp"
 
 namespace stdspec {
 namespace {
@@ -42,43 +43,6 @@ struct KeyList {
     if (!sparse || e < vis_start) return e;
     const int t = e - vis_start;
     return t < topk ? idx[t] : vis_end + (t - topk);
-  }
-};
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-__device__ __forceinline__ floatx4_t mfma_bf16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-// ds_read_b64_tr_b16: within each 16-lane group the lanes' 8-byte rows form
-// M[16][4]; lane i receives {M[4j + i/4][i%4] : j = 0..3}.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
-  const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
-  return __builtin_bit_cast(uint2, t);
-}
-
-// LDS tiles of 64 K or V rows, row-major, with the 16-byte chunks of each
-// row permuted (XOR swizzle) so that the reads feeding one MFMA operand hit
-// distinct banks:
-//  * K: chunk c of row r sits at slot c ^ (r % CPR).  A K-operand read takes
-//    one chunk of 16 consecutive rows.
-//  * V: chunk c of row r sits at slot c ^ 2*(r % 4).  A transpose read takes
-//    8 bytes from 4 consecutive rows x 2 chunks per 16 lanes; the XOR with
-//    2*(r % 4) spreads those over 8 distinct slots.
-template <int D>
-struct Tile {
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static __device__ __forceinline__ int slot_k(int row, int chunk) { return chunk ^ (row % CPR); }
-  static __device__ __forceinline__ int slot_v(int row, int chunk) { return chunk ^ ((row & 3) << 1); }
-  static __device__ __forceinline__ int off_k(int row, int chunk) {   // elements
-    return row * D + (slot_k(row, chunk) << 3);
-  }
-  static __device__ __forceinline__ int off_v(int row, int chunk) {
-    return row * D + (slot_v(row, chunk) << 3);
   }
 };
 
@@ -203,21 +167,6 @@ __device__ __forceinline__ void stage_store(const u32x4_t (&kr)[KPT], const u32x
     *reinterpret_cast<u32x4_t*>(ks + rrow[u] * D + (rslot[u] << 3)) = kr[u];
     *reinterpret_cast<u32x4_t*>(vs + rrow[u] * D + (rslot[u] << 3)) = vr[u];
   }
-}
-
-// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
-// l^48) with the gfx950 cross-row permutes, no LDS round trip.
-__device__ __forceinline__ float max_over_groups(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_over_groups(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Dense verify, one wave's share of a 64-key tile: the 32 keys of key half

@@ -18,6 +18,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "tile.hpp"
 
 namespace stdspec {
 namespace {
@@ -26,11 +27,6 @@ constexpr int kLseChunk = 8192;     // keys per workgroup in step 1 (MFMA)
 constexpr int kRowsPerLseWg = 128;  // text rows per workgroup in step 1
 constexpr int kColsPerScoreWg = 256;  // visual keys per workgroup in step 2
 constexpr int kXcds = 8;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-__device__ __forceinline__ floatx4_t mfma_bf16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (each with its
 // own L2).  Map them so that each XCD receives a contiguous run of work
@@ -48,20 +44,95 @@ struct Geo {
   float c;  // scale * log2 e
 };
 
+// Stage one 64-row tile of a [rows][D] bf16 tensor: global -> registers
+// (rows clamped to ``last``, so every load is in bounds) and registers ->
+// LDS in the K-swizzled layout of Tile<D>.
+template <int D, int KPT>
+__device__ __forceinline__ void tile_load(u32x4_t (&r)[KPT], const uint16_t* base, int row0,
+                                          int last, const int (&rrow)[KPT],
+                                          const int (&rslot)[KPT]) {
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const size_t off = (size_t)min(row0 + rrow[u], last) * D;
+    r[u] = *reinterpret_cast<const u32x4_t*>(base + off + (Tile<D>::slot_k(rrow[u], rslot[u]) << 3));
+  }
+}
+template <int D, int KPT>
+__device__ __forceinline__ void tile_store(const u32x4_t (&r)[KPT], uint16_t* lds,
+                                           const int (&rrow)[KPT], const int (&rslot)[KPT]) {
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    *reinterpret_cast<u32x4_t*>(lds + rrow[u] * D + (rslot[u] << 3)) = r[u];
+}
+
 // ---------------------------------------------------------------------------
 // Step 1 (bf16, MFMA): partial (max, sum) of each text row over one key chunk.
 // Work item = (KV head, key chunk, 128-row block); 4 waves x 32 rows.  Keys
-// are staged in LDS (64 per tile) and are the M side of S^T = K Q^T, rows
+// are staged in LDS (64 per tile, double buffered, the next tiles' loads in
+// flight in two register buffers) and are the M side of S^T = K Q^T, rows
 // the N side.  Each lane keeps its own running (max, fp64 sum) over the keys
-// it sees; the four lanes of a column are merged once at the end.
+// it sees; the max moves only when a score exceeds it by 2^8 (exact: it is
+// only the shift of the exponent), and the four lanes of a column are merged
+// once at the end.  Only tiles that reach the causal (text) part or the
+// chunk end are masked.
 template <int D>
-__global__ __launch_bounds__(256) void lse_partial_mfma(const uint16_t* __restrict__ qt,
-                                                        const uint16_t* __restrict__ k, Geo geo,
-                                                        int n_chunks, int n_rb,
-                                                        float* __restrict__ m_part,
-                                                        double* __restrict__ l_part) {
-  constexpr int KST = D / 32, KP = D + 8, CPR = D / 8, KPT = D / 32;
-  __shared__ __align__(16) uint16_t Ks[64 * KP];
+__device__ __forceinline__ void lse_tile(const uint16_t* Ks, const bf16x8_t (*qb)[D / 32],
+                                         int t0, int key1, int text_start, const int* rpos,
+                                         float c, int col, int grp, float* m, double* l) {
+  constexpr int KST = D / 32;
+  floatx4_t sacc[4][2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    u32x4_t a[KST];
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      a[kk] = *reinterpret_cast<const u32x4_t*>(Ks + Tile<D>::off_k(kb * 16 + col, KST * grp + kk));
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kk]), qb[nb][kk], acc);
+      sacc[kb][nb] = acc;
+    }
+  }
+  const bool masked = t0 + 64 > text_start || t0 + 64 > key1;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = sacc[j >> 2][nb][j & 3];
+    if (masked) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = t0 + (j >> 2) * 16 + 4 * grp + (j & 3);
+        if (!(key < key1 && key <= rpos[nb])) v[j] = -INFINITY;
+      }
+    }
+    float tmax = v[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, v[j]);
+    if (tmax == -INFINITY) continue;
+    const float ts = tmax * c;                       // c > 0: max then scale
+    if (ts > m[nb] + 8.f) {
+      if (m[nb] != -INFINITY) l[nb] *= exp2((double)m[nb] - (double)ts);
+      m[nb] = ts;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ps += fast_exp2(fmaf(v[j], c, -m[nb]));
+    l[nb] += (double)ps;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void lse_partial_mfma(const uint16_t* __restrict__ qt,
+                                                           const uint16_t* __restrict__ k, Geo geo,
+                                                           int n_chunks, int n_rb,
+                                                           float* __restrict__ m_part,
+                                                           double* __restrict__ l_part) {
+  constexpr int KST = D / 32, CPR = D / 8, KPT = 64 * CPR / 256;
+  __shared__ __align__(16) uint16_t Ks0[64 * D];
+  __shared__ __align__(16) uint16_t Ks1[64 * D];
   const int n_items = geo.hkv * n_chunks * n_rb;
   const int item = xcd_item(blockIdx.x, n_items);
   if (item >= n_items) return;
@@ -75,7 +146,6 @@ __global__ __launch_bounds__(256) void lse_partial_mfma(const uint16_t* __restri
   const int n_keys = geo.text_start + geo.n_text;
   const int key0 = ch * kLseChunk, key1 = min(n_keys, key0 + kLseChunk);
 
-  // two 16-row column blocks per wave
   bf16x8_t qb[2][KST];
   int rpos[2];
   bool rok[2];
@@ -96,66 +166,35 @@ __global__ __launch_bounds__(256) void lse_partial_mfma(const uint16_t* __restri
   double l[2] = {0.0, 0.0};
 
   const uint16_t* kh = k + (size_t)g * geo.capacity * D;
-  uint4 kreg[KPT];
-  auto load_tile = [&](int t0) {
+  int rrow[KPT], rslot[KPT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cl = tid + 256 * u;
-      const int key = t0 + cl / CPR;
-      kreg[u] = key < key1 ? *reinterpret_cast<const uint4*>(kh + (size_t)key * D + (cl % CPR) * 8)
-                           : make_uint4(0, 0, 0, 0);
-    }
-  };
+  for (int u = 0; u < KPT; ++u) {
+    const int cl = tid + 256 * u;
+    rrow[u] = cl / CPR;
+    rslot[u] = cl % CPR;
+  }
   const int ntiles = (key1 - key0 + 63) / 64;
-  load_tile(key0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = key0 + t * 64;
+  u32x4_t ra[KPT], rb_[KPT];
+  tile_load<D, KPT>(ra, kh, key0, key1 - 1, rrow, rslot);
+  tile_store<D, KPT>(ra, Ks0, rrow, rslot);
+  tile_load<D, KPT>(ra, kh, key0 + 64, key1 - 1, rrow, rslot);
+  tile_load<D, KPT>(rb_, kh, key0 + 128, key1 - 1, rrow, rslot);
+  for (int t = 0; t < ntiles; t += 2) {
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cl = tid + 256 * u;
-      *reinterpret_cast<uint4*>(Ks + (cl / CPR) * KP + (cl % CPR) * 8) = kreg[u];
-    }
+    tile_store<D, KPT>(ra, Ks1, rrow, rslot);
+    tile_load<D, KPT>(ra, kh, key0 + (t + 3) * 64, key1 - 1, rrow, rslot);
+    lse_tile<D>(Ks0, qb, key0 + t * 64, key1, geo.text_start, rpos, geo.c, col, grp, m, l);
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t0 + 64);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float x[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KST; ++kk) {
-          const uint4 a = *reinterpret_cast<const uint4*>(Ks + (kb * 16 + col) * KP +
-                                                          (D / 4) * grp + 8 * kk);
-          acc = mfma_bf16(as_bf16x8(a), qb[nb][kk], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t0 + kb * 16 + 4 * grp + i;
-          const float xv = (key < key1 && key <= rpos[nb]) ? acc[i] * geo.c : -INFINITY;
-          x[kb * 4 + i] = xv;
-          tmax = fmaxf(tmax, xv);
-        }
-      }
-      if (tmax == -INFINITY) continue;
-      if (tmax > m[nb]) {
-        if (m[nb] != -INFINITY) l[nb] *= exp2((double)m[nb] - (double)tmax);
-        m[nb] = tmax;
-      }
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ps += fast_exp2(x[j] - m[nb]);
-      l[nb] += (double)ps;
-    }
+    tile_store<D, KPT>(rb_, Ks0, rrow, rslot);
+    tile_load<D, KPT>(rb_, kh, key0 + (t + 4) * 64, key1 - 1, rrow, rslot);
+    if (t + 1 < ntiles)
+      lse_tile<D>(Ks1, qb, key0 + (t + 1) * 64, key1, geo.text_start, rpos, geo.c, col, grp, m,
+                  l);
   }
   // merge the four lanes of each column, then write this chunk's partial
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float mm = m[nb];
-    mm = fmaxf(mm, __shfl_xor(mm, 16, kWave));
-    mm = fmaxf(mm, __shfl_xor(mm, 32, kWave));
+    const float mm = max_over_groups(m[nb]);
     double ll = (m[nb] == -INFINITY) ? 0.0 : l[nb] * exp2((double)m[nb] - (double)mm);
     ll += __shfl_xor(ll, 16, kWave);
     ll += __shfl_xor(ll, 32, kWave);
@@ -218,18 +257,20 @@ __global__ __launch_bounds__(64) void lse_valu(const T* __restrict__ qt, const T
 // ---------------------------------------------------------------------------
 // Step 2 (bf16, MFMA): column sums over all text rows of the group for 256
 // visual keys.  S = Q K^T with rows on the M side (streamed through LDS, 64
-// per tile) and keys on the N side (4 blocks of 16 per wave, held in
-// registers).  Each lane owns one key per block and sums its rows; the four
-// lanes of a key are merged at the end, in fp64.
+// per tile, double buffered) and keys on the N side (4 blocks of 16 per
+// wave, held in registers).  Each lane owns one key per block and sums its
+// rows; partial sums of a tile are fp32 and are added into fp64
+// accumulators; the four lanes of a key are merged at the end in fp64.
 template <int D>
-__global__ __launch_bounds__(256) void colscore_mfma(const uint16_t* __restrict__ qt,
-                                                     const uint16_t* __restrict__ k, Geo geo,
-                                                     const float* __restrict__ lse,
-                                                     float lse_factor, int n_ct,
-                                                     float* __restrict__ scores) {
-  constexpr int KST = D / 32, KP = D + 8, CPR = D / 8, KPT = D / 32;
-  __shared__ __align__(16) uint16_t Qs[64 * KP];
-  __shared__ float Ls[64];
+__global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restrict__ qt,
+                                                        const uint16_t* __restrict__ k, Geo geo,
+                                                        const float* __restrict__ lse,
+                                                        float lse_factor, int n_ct,
+                                                        float* __restrict__ scores) {
+  constexpr int KST = D / 32, CPR = D / 8, KPT = 64 * CPR / 256;
+  __shared__ __align__(16) uint16_t Qs0[64 * D];
+  __shared__ __align__(16) uint16_t Qs1[64 * D];
+  __shared__ float Ls[2][64];
   const int n_items = geo.hkv * n_ct;
   const int item = xcd_item(blockIdx.x, n_items);
   if (item >= n_items) return;
@@ -239,73 +280,81 @@ __global__ __launch_bounds__(256) void colscore_mfma(const uint16_t* __restrict_
   const int col = lane & 15, grp = lane >> 4;
   const int R = geo.G * geo.n_text;
 
-  // key operands: B[k = d][n = key], key = base + kb*16 + col
+  // key operands: B[k = d][n = key], key = base + kb*16 + col (clamped)
   bf16x8_t kbop[4][KST];
   const uint16_t* kh = k + (size_t)g * geo.capacity * D;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const int j = ct * kColsPerScoreWg + wave * 64 + kb * 16 + col;
-    const bool ok = j < geo.vis_len;
-    const uint16_t* krow = kh + (size_t)(geo.vis_start + (ok ? j : 0)) * D + (D / 4) * grp;
+    const int j = min(ct * kColsPerScoreWg + wave * 64 + kb * 16 + col, geo.vis_len - 1);
+    const uint16_t* krow = kh + (size_t)(geo.vis_start + j) * D + (D / 4) * grp;
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = *reinterpret_cast<const uint4*>(krow + 8 * kk);
-      kbop[kb][kk] = as_bf16x8(u);
-    }
+    for (int kk = 0; kk < KST; ++kk)
+      kbop[kb][kk] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(krow + 8 * kk));
   }
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
 
   const uint16_t* qg = qt + (size_t)g * R * D;
-  uint4 qreg[KPT];
-  float lreg = 0.f;
-  auto load_tile = [&](int r0) {
+  const float* lg = lse + (size_t)g * R;
+  int rrow[KPT], rslot[KPT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cl = tid + 256 * u;
-      const int row = r0 + cl / CPR;
-      qreg[u] = row < R ? *reinterpret_cast<const uint4*>(qg + (size_t)row * D + (cl % CPR) * 8)
-                        : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < 64) {
-      const int row = r0 + tid;
-      lreg = row < R ? lse[(size_t)g * R + row] * lse_factor : INFINITY;
-    }
-  };
-  const int ntiles = (R + 63) / 64;
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
+  for (int u = 0; u < KPT; ++u) {
+    const int cl = tid + 256 * u;
+    rrow[u] = cl / CPR;
+    rslot[u] = cl % CPR;
+  }
+  // row normalisers: rows past the end get +inf (probability 0)
+  auto lse_of = [&](int row) { return row < R ? lg[row] * lse_factor : INFINITY; };
+
+  // one 64-row tile: four 16-row blocks; a block's 16 MFMAs are issued
+  // before the previous block's exponentials are summed
+  auto tile = [&](const uint16_t* Qs, const float* L) {
+    float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cl = tid + 256 * u;
-      *reinterpret_cast<uint4*>(Qs + (cl / CPR) * KP + (cl % CPR) * 8) = qreg[u];
-    }
-    if (tid < 64) Ls[tid] = lreg;
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile((t + 1) * 64);
-    float lrow[4][4];
+    for (int qb = 0; qb < 4; ++qb) {
+      u32x4_t a[KST];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+      for (int kk = 0; kk < KST; ++kk)
+        a[kk] = *reinterpret_cast<const u32x4_t*>(Qs + Tile<D>::off_k(qb * 16 + col, KST * grp + kk));
+      float lrow[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lrow[qb][i] = Ls[qb * 16 + 4 * grp + i];
+      for (int i = 0; i < 4; ++i) lrow[i] = L[qb * 16 + 4 * grp + i];
+      floatx4_t sv[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float cs = 0.f;
+      for (int kb = 0; kb < 4; ++kb) {
+        floatx4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KST; ++kk) {
-          const uint4 a = *reinterpret_cast<const uint4*>(Qs + (qb * 16 + col) * KP +
-                                                          (D / 4) * grp + 8 * kk);
-          s = mfma_bf16(as_bf16x8(a), kbop[kb][kk], s);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cs += fast_exp2(fmaf(s[i], geo.c, -lrow[qb][i]));
+        for (int kk = 0; kk < KST; ++kk) x = mfma_bf16(as_bf16x8(a[kk]), kbop[kb][kk], x);
+        sv[kb] = x;
       }
-      acc[kb] += (double)cs;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[kb] += fast_exp2(fmaf(sv[kb][i], geo.c, -lrow[i]));
     }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] += (double)cs[kb];
+  };
+
+  const int ntiles = (R + 63) / 64;
+  u32x4_t ra[KPT], rb_[KPT];
+  float la = 0.f, lb = 0.f;
+  tile_load<D, KPT>(ra, qg, 0, R - 1, rrow, rslot);
+  tile_store<D, KPT>(ra, Qs0, rrow, rslot);
+  if (tid < 64) Ls[0][tid] = lse_of(tid);
+  tile_load<D, KPT>(ra, qg, 64, R - 1, rrow, rslot);
+  tile_load<D, KPT>(rb_, qg, 128, R - 1, rrow, rslot);
+  if (tid < 64) { la = lse_of(64 + tid); lb = lse_of(128 + tid); }
+  for (int t = 0; t < ntiles; t += 2) {
+    __syncthreads();
+    tile_store<D, KPT>(ra, Qs1, rrow, rslot);
+    if (tid < 64) { Ls[1][tid] = la; la = lse_of((t + 3) * 64 + tid); }
+    tile_load<D, KPT>(ra, qg, (t + 3) * 64, R - 1, rrow, rslot);
+    tile(Qs0, Ls[0]);
+    __syncthreads();
+    tile_store<D, KPT>(rb_, Qs0, rrow, rslot);
+    if (tid < 64) { Ls[0][tid] = lb; lb = lse_of((t + 4) * 64 + tid); }
+    tile_load<D, KPT>(rb_, qg, (t + 4) * 64, R - 1, rrow, rslot);
+    if (t + 1 < ntiles) tile(Qs1, Ls[1]);
   }
   const double inv = 1.0 / ((double)geo.G * (double)geo.n_text);
 #pragma unroll
