@@ -46,18 +46,19 @@ struct KeyList {
   }
 };
 
-// One 64-key tile for one wave's 16 query columns.
-template <int D>
+// One tile of 16*NKB keys (NKB = 1, 2 or 4 key blocks) for one wave's 16
+// query columns.
+template <int D, int NKB>
 struct TileMath {
   static constexpr int KST = D / 32;   // 32-wide contraction steps over d
   static constexpr int DB = D / 16;    // 16-wide output blocks over d
 
-  // S^T = K Q^T for the 4 key blocks: lane (col, grp) gets keys
+  // S^T = K Q^T for the NKB key blocks: lane (col, grp) gets keys
   // kb*16 + 4*grp + i of query column col.
   static __device__ __forceinline__ void scores(const uint16_t* Ks, const bf16x8_t* qb,
                                                 int col, int grp, floatx4_t* sacc) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
@@ -69,21 +70,28 @@ struct TileMath {
     }
   }
 
-  // O^T += V^T P^T over the tile's 64 keys in two 32-key steps.  The B
-  // operand holds the lane's own probabilities (keys 32ks + 4grp + j and
+  // O^T += V^T P^T over the tile's keys in 32-key steps.  The B operand
+  // holds the lane's own probabilities (keys 32ks + 4grp + j and
   // 32ks + 16 + 4grp + j); the A operand (V^T, lane = d row) is read from the
   // row-major V tile with two transpose reads whose per-lane row addresses
-  // follow the same key order.
+  // follow the same key order.  With a single key block the upper 16 keys
+  // of the step are absent: their operand halves are zero.
   static __device__ __forceinline__ void pv(const uint16_t* Vs, const float* p, int col,
                                             int grp, floatx4_t* oacc) {
     const int r4 = col >> 2, rc = col & 3;
+    constexpr int NKS = NKB >= 2 ? NKB / 2 : 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       uint4 pw;
       pw.x = pack_bf16x2(p[(2 * ks) * 4 + 0], p[(2 * ks) * 4 + 1]);
       pw.y = pack_bf16x2(p[(2 * ks) * 4 + 2], p[(2 * ks) * 4 + 3]);
-      pw.z = pack_bf16x2(p[(2 * ks + 1) * 4 + 0], p[(2 * ks + 1) * 4 + 1]);
-      pw.w = pack_bf16x2(p[(2 * ks + 1) * 4 + 2], p[(2 * ks + 1) * 4 + 3]);
+      if constexpr (NKB >= 2) {
+        pw.z = pack_bf16x2(p[(2 * ks + 1) * 4 + 0], p[(2 * ks + 1) * 4 + 1]);
+        pw.w = pack_bf16x2(p[(2 * ks + 1) * 4 + 2], p[(2 * ks + 1) * 4 + 3]);
+      } else {
+        pw.z = 0u;
+        pw.w = 0u;
+      }
       const bf16x8_t pb = as_bf16x8(pw);
       const int row0 = 32 * ks + 4 * grp + r4;
 #pragma unroll
@@ -91,26 +99,27 @@ struct TileMath {
         const int chunk = 2 * db + (rc >> 1);
         const int e = 4 * (rc & 1);
         const uint2 lo = lds_read_tr16(Vs + Tile<D>::off_v(row0, chunk) + e);
-        const uint2 hi = lds_read_tr16(Vs + Tile<D>::off_v(row0 + 16, chunk) + e);
+        uint2 hi = make_uint2(0u, 0u);
+        if constexpr (NKB >= 2) hi = lds_read_tr16(Vs + Tile<D>::off_v(row0 + 16, chunk) + e);
         oacc[db] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, oacc[db]);
       }
     }
   }
 };
 
-// Online softmax for one tile: x holds 16 base-2 scores (-inf when masked).
+// Online softmax for one tile: x holds NJ base-2 scores (-inf when masked).
 // The running max m of a column moves only when a score exceeds it by more
 // than 2^8 (or m is unset); probabilities are taken relative to m, so they
 // stay below 256 and the accumulator rescale (AGPR round trips) is skipped
 // on almost every tile.  Exact: m is only a shift of the exponent.
 constexpr float kLazyMax = 8.f;
 
-template <int DB>
+template <int DB, int NJ>
 __device__ __forceinline__ void online_update(const float* x, float* p, float& m, float& lsum,
                                               floatx4_t* oacc) {
   float tmax = x[0];
 #pragma unroll
-  for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
+  for (int j = 1; j < NJ; ++j) tmax = fmaxf(tmax, x[j]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
   if (tmax > m + kLazyMax) {            // also taken while m is still -inf
@@ -123,7 +132,7 @@ __device__ __forceinline__ void online_update(const float* x, float* p, float& m
   const float msafe = (m == -INFINITY) ? 0.f : m;
   float psum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     p[j] = fast_exp2(x[j] - msafe);
     psum += p[j];
   }
@@ -404,28 +413,39 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Sparse draft step: grid (split of 256 key-list entries, KV head), 4 waves.
+// Sparse draft step: grid (split of kSparseChunk key-list entries, KV head),
+// kSparseWaves waves of kSparseEntriesPerWave entries each.
 //
-// Each wave gathers one 64-entry tile of the head's key list (prefix +
-// selected visual positions + tail) into its own LDS region -- one
-// contiguous 256-byte row per 16 lanes, all loads issued before any is used
-// -- and reduces it for the G <= 16 query heads of the group (one MFMA
-// column block).  The four waves merge in LDS and the workgroup writes one
-// (max, sum, output) partial for the combine pass.
-constexpr int kSparseWaves = 4;
+// Each wave gathers its entries of the head's key list (prefix + selected
+// visual positions + tail) into its own LDS region -- one contiguous
+// 256-byte row per 16 lanes, all loads issued before any is used -- and
+// reduces them for the G <= 16 query heads of the group (one MFMA column
+// block).  The waves merge in LDS and the workgroup writes one
+// (max, sum, output) partial for the combine pass.  Splits are small so the
+// grid covers the chip: the step moves only a few MB and is bound by the
+// latency of the index load -> row gather -> reduce chain, which every
+// workgroup runs once.
+constexpr int kSparseWaves = kSparseChunk / kSparseEntriesPerWave;
 
 template <int D>
-__global__ __launch_bounds__(256) void sparse_mfma_kernel(
+__global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, int n_entries,
     int splits, float2* __restrict__ ml, float* __restrict__ o) {
-  using TM = TileMath<D>;
+  constexpr int EW = kSparseEntriesPerWave;
+  constexpr int NKB = EW / 16;
+  using TM = TileMath<D, NKB>;
   constexpr int DB = TM::DB;
-  constexpr int CPR = D / 8;          // chunks per row == loads per lane per tensor
-  constexpr int TILE = 64 * D;
-  __shared__ __align__(16) uint16_t smem[kSparseWaves * 2 * TILE];
-  __shared__ int pos_s[kSparseWaves * 64];
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int NL = EW * CPR / 64;   // loads per lane per tensor
+  constexpr int REGION = EW * D;      // elements of one wave's K (or V) tile
+  constexpr int XS = 2 + 4 * DB;      // floats per lane in the merge
+  constexpr int STAGE = kSparseWaves * 2 * REGION * 2;
+  constexpr int XCH = kSparseWaves * 64 * XS * 4;
+  __shared__ __align__(16) uint8_t smem_raw[STAGE > XCH ? STAGE : XCH];
+  __shared__ int pos_s[kSparseChunk];
+  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const int s = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -433,21 +453,28 @@ __global__ __launch_bounds__(256) void sparse_mfma_kernel(
   const int col = lane & 15, grp = lane >> 4;
   const bool row_ok = col < G;
   const int h = g * G + (row_ok ? col : 0);
-  uint16_t* Ks = smem + wave * 2 * TILE;
-  uint16_t* Vs = Ks + TILE;
-  int* pw = pos_s + wave * 64;
+  uint16_t* Ks = smem + wave * 2 * REGION;
+  uint16_t* Vs = Ks + REGION;
+  int* pw = pos_s + wave * EW;
 
   KeyList kl{true, idx + (size_t)g * topk, vis_start, vis_end, topk};
-  const int e = s * (64 * kSparseWaves) + wave * 64 + lane;
-  pw[lane] = e < n_entries ? kl.pos(e) : -1;
-  __syncthreads();
+  const int e0 = s * kSparseChunk + wave * EW;   // first entry of this wave
+  if (lane < EW) {
+    const int e = e0 + lane;
+    pw[lane] = e < n_entries ? kl.pos(e) : -1;
+  }
+  bf16x8_t qb[D / 32];
+  load_q_operand<D>(q + (size_t)h * D, row_ok, grp, qb);
+  // pw is written and read by this wave only
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
 
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
   const int last = kl.pos(n_entries - 1);   // a valid row for the padded entries
-  u32x4_t kreg[CPR], vreg[CPR];
+  u32x4_t kreg[NL], vreg[NL];
 #pragma unroll
-  for (int u = 0; u < CPR; ++u) {
+  for (int u = 0; u < NL; ++u) {
     const int cl = lane + 64 * u;
     const int row = cl / CPR, slot = cl % CPR;
     int pr = pw[row];
@@ -456,10 +483,8 @@ __global__ __launch_bounds__(256) void sparse_mfma_kernel(
     kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base + (Tile<D>::slot_k(row, slot) << 3));
     vreg[u] = *reinterpret_cast<const u32x4_t*>(vh + base + (Tile<D>::slot_v(row, slot) << 3));
   }
-  bf16x8_t qb[D / 32];
-  load_q_operand<D>(q + (size_t)h * D, row_ok, grp, qb);
 #pragma unroll
-  for (int u = 0; u < CPR; ++u) {
+  for (int u = 0; u < NL; ++u) {
     const int cl = lane + 64 * u;
     *reinterpret_cast<u32x4_t*>(Ks + (cl / CPR) * D + ((cl % CPR) << 3)) = kreg[u];
     *reinterpret_cast<u32x4_t*>(Vs + (cl / CPR) * D + ((cl % CPR) << 3)) = vreg[u];
@@ -472,23 +497,22 @@ __global__ __launch_bounds__(256) void sparse_mfma_kernel(
   floatx4_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  if (s * (64 * kSparseWaves) + wave * 64 < n_entries) {
-    floatx4_t sacc[4];
+  if (e0 < n_entries) {
+    floatx4_t sacc[NKB];
     TM::scores(Ks, qb, col, grp, sacc);
-    float x[16], p[16];
+    float x[4 * NKB], p[4 * NKB];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < 4 * NKB; ++j)
       x[j] = pw[(j >> 2) * 16 + 4 * grp + (j & 3)] >= 0 ? sacc[j >> 2][j & 3] * c : -INFINITY;
-    online_update<DB>(x, p, m, lsum, oacc);
+    online_update<DB, 4 * NKB>(x, p, m, lsum, oacc);
     TM::pv(Vs, p, col, grp, oacc);
   }
   lsum = sum_over_groups(lsum);
 
-  // merge the four waves: each lane's (m, l, 4*DB outputs) through LDS
-  constexpr int XS = 2 + 4 * DB;
-  float* xch = reinterpret_cast<float*>(smem);
+  // merge the waves: each lane's (m, l, 4*DB outputs) through LDS
+  float* xch = reinterpret_cast<float*>(smem_raw);
   __syncthreads();                     // every wave is done with its tile
-  {
+  if (wave > 0) {
     float* dst = xch + (size_t)(wave * 64 + lane) * XS;
     dst[0] = m;
     dst[1] = lsum;
@@ -500,19 +524,21 @@ __global__ __launch_bounds__(256) void sparse_mfma_kernel(
   __syncthreads();
   if (wave == 0) {
     float mw[kSparseWaves];
-    float M = -INFINITY;
+    mw[0] = m;
+    float M = m;
 #pragma unroll
-    for (int w = 0; w < kSparseWaves; ++w) {
+    for (int w = 1; w < kSparseWaves; ++w) {
       mw[w] = xch[(size_t)(w * 64 + lane) * XS];
       M = fmaxf(M, mw[w]);
     }
     const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
+    const float a0 = fast_exp2(mw[0] - Ms);
+    float L = lsum * a0;
     floatx4_t acc[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DB; ++db) acc[db] = oacc[db] * a0;
 #pragma unroll
-    for (int w = 0; w < kSparseWaves; ++w) {
+    for (int w = 1; w < kSparseWaves; ++w) {
       const float* src = xch + (size_t)(w * 64 + lane) * XS;
       const float a = fast_exp2(mw[w] - Ms);
       L = fmaf(src[1], a, L);
@@ -695,7 +721,7 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   if (a.sparse) {
     const int n_entries = sparse_list_len(a.len, a.vis_start, a.vis_len, a.topk);
-    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv), 256, 0, st>>>(
+    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv), 64 * kSparseWaves, 0, st>>>(
         q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
         a.topk, n_entries, a.splits, reinterpret_cast<float2*>(a.ml), a.o);
   } else {

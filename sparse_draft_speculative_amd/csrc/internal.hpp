@@ -30,8 +30,10 @@ inline int dense_split_count(int len, int n_kv_heads) {
 }
 
 // Sparse decode: the per-head key list (prefix + selected + tail) is cut
-// into splits of 256 entries (four 64-entry tiles, one wave each).
-constexpr int kSparseChunk = 256;
+// into splits of kSparseChunk entries, kSparseEntriesPerWave per wave
+// (16, 32 or 64: one to four 16-key MFMA blocks).
+constexpr int kSparseEntriesPerWave = 32;
+constexpr int kSparseChunk = 128;
 
 inline int sparse_list_len(int len, int vis_start, int vis_len, int topk) {
   return vis_start + topk + (len - (vis_start + vis_len));
