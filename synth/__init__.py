@@ -207,6 +207,12 @@ TOY_C5 = dict(n_layers=4, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64,
               mlp=1536, vocab=8192, eps=1e-6, rope_theta=1e4,
               n_vis=8192, n_text=128, salient_frac=0.05, topk=512)
 
+# a small decoder the GPU kernels take (head_dim 64) and the float64
+# oracle still runs in seconds
+TOY_GPU = dict(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+               mlp=512, vocab=512, eps=1e-6, rope_theta=1e4,
+               n_vis=1024, n_text=32, salient_frac=0.05, topk=64)
+
 TOY_TINY = dict(n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16,
                 mlp=128, vocab=256, eps=1e-6, rope_theta=1e4,
                 n_vis=256, n_text=16, salient_frac=0.05, topk=32)

@@ -1,0 +1,105 @@
+"""End to end on the GPU: a small decoder whose attention runs on the four
+calls (sparse_draft_speculative_amd.toy_decoder), in fp32.
+
+Pins (the pages' Key contributions: the acceleration is lossless, the output
+is that of the dense model):
+  * the GPU's dense-only greedy stream equals the float64 oracle's greedy
+    stream on the same weights;
+  * the GPU's StD stream equals the GPU's dense-only stream, for several K
+    and gamma;
+  * with K = vis_len the draft model is the dense model, so every cycle
+    accepts all gamma drafts.
+Streams are compared up to the first position whose dense argmax margin is
+<= 1e-3 (where two correct implementations may pick different tokens);
+every stream here is checked to reach well past the first few tokens.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import toy as oracle_toy
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-3
+N_NEW = 40
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_draft_speculative_amd as sd
+    from sparse_draft_speculative_amd.toy_decoder import ToyDecoder
+    sd.load()
+    cfg = dict(synth.TOY_GPU)
+    params = synth.toy_params(cfg, seed=3, std=0.1)
+    vis, text = synth.toy_prompt(cfg, seed=3)
+    prompt_len = cfg["n_vis"] + cfg["n_text"]
+    dec = ToyDecoder(params, prompt_len + N_NEW + 16, dtype=torch.float32, prefill_chunk=256)
+    margins = torch.full((N_NEW,), float("inf"), dtype=torch.float32, device="cuda")
+    first, q_text = dec.prefill(vis, text, margin=margins[0:1])
+    snap = dec.snapshot()
+    dense = dec.decode_dense(first, prompt_len, N_NEW, margins=margins)
+    torch.cuda.synchronize()
+    return dict(cfg=cfg, params=params, vis=vis, text=text, dec=dec, first=first,
+                q_text=q_text, snap=snap, dense=dense, margins=margins.cpu().numpy(),
+                prompt_len=prompt_len)
+
+
+def trusted_prefix(margins):
+    """Positions before the first dense argmax margin <= MARGIN."""
+    low = np.nonzero(margins <= MARGIN)[0]
+    return int(low[0]) if low.size else len(margins)
+
+
+def test_dense_stream_matches_oracle_greedy(setup):
+    s = setup
+    ref = oracle_toy.toy_greedy(s["params"], s["vis"], s["text"], N_NEW)
+    n = trusted_prefix(s["margins"])
+    say(f"dense stream: trusted prefix {n} of {N_NEW}")
+    assert n >= 8
+    assert s["dense"][:n] == ref[:n]
+
+
+@pytest.mark.parametrize("topk,gamma", [(64, 4), (16, 2), (256, 6)])
+def test_std_stream_equals_dense_stream(setup, topk, gamma):
+    s = setup
+    cfg, dec = s["cfg"], s["dec"]
+    dec.restore(s["snap"])
+    idx = dec.select(s["q_text"], s["prompt_len"], 0, cfg["n_vis"], topk)
+    out, acc = dec.decode_std(s["first"], s["prompt_len"], N_NEW, idx, 0, cfg["n_vis"], gamma)
+    n = trusted_prefix(s["margins"])
+    say(f"K={topk} gamma={gamma}: accepted per cycle {acc}; trusted prefix {n}")
+    assert all(0 <= a <= gamma for a in acc)
+    assert out[:n] == s["dense"][:n]
+
+
+def test_full_selection_accepts_every_draft(setup):
+    """K = vis_len: sparse key set == dense key set (the pages' special
+    case), so each cycle accepts all gamma drafts while the dense margins
+    are clear of the tie band."""
+    s = setup
+    cfg, dec = s["cfg"], s["dec"]
+    gamma = 4
+    dec.restore(s["snap"])
+    idx = dec.select(s["q_text"], s["prompt_len"], 0, cfg["n_vis"], cfg["n_vis"])
+    out, acc = dec.decode_std(s["first"], s["prompt_len"], N_NEW, idx, 0, cfg["n_vis"], gamma)
+    n = trusted_prefix(s["margins"])
+    say(f"K=vis_len: accepted per cycle {acc}; trusted prefix {n}")
+    assert out[:n] == s["dense"][:n]
+    pos = 1                                  # stream index of the first draft
+    for a in acc:
+        if pos + gamma > n:                  # cycle reaches the tie band
+            break
+        assert a == gamma
+        pos += a + 1
