@@ -35,8 +35,12 @@ import os
 import sys
 import time
 
+import numpy as np
+
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
+CPU_LAYERS = 4             # layers of the workload the CPU baseline samples
+CPU_ROWS = 384             # text rows per sampled layer for the CPU selection
 METRIC = "sparse/dense attn HBM GB/s (% of peak) + draft-verify tokens/sec @140k ctx"
 
 
@@ -50,6 +54,8 @@ def parse():
     ap.add_argument("--alpha", type=float, default=0.95)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense-tokens", type=int, default=8)
+    ap.add_argument("--no-toy", action="store_true",
+                    help="skip the end-to-end toy decoder measurement")
     return ap.parse_args()
 
 
@@ -97,6 +103,8 @@ def main():
     for lay in layers:
         lay.pop("planted")
     torch.cuda.synchronize()
+    cpu_layers = [] if args.no_cpu_baseline else [
+        {k_: t_.cpu() for k_, t_ in layers[l].items()} for l in range(min(CPU_LAYERS, L))]
 
     # ---------------------------------------------------------------- setup
     shape = sd.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
@@ -267,52 +275,115 @@ def main():
         "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
         "dense_only_attn_gbps": round(dense_gbps, 1),
     }
+    if not args.no_toy:
+        line["toy_e2e"] = toy_e2e()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, layers[0], args, cycles / args.steps)
+        line["cpu_baseline"] = cpu_baseline(cfg, cpu_layers, args, cycles / args.steps)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, lay, args, cycles_per_request):
+def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
+    """Draft-verify decoding of a random-init toy decoder, measured end to end.
+
+    Decoder: 4 layers, hidden 512, 8 query / 2 KV heads of 64, SwiGLU MLP
+    1,536, vocab 8,192, bf16 weights N(0, 0.02^2) and cache; prompt = 8,192
+    synthetic visual embeddings (5% carry a planted direction) + 128 random
+    text ids; K = 512.  Every attention runs on the library; the rest of the
+    model is torch.  Tokens/s counts tokens 2..n_new (token 1 comes from the
+    prefill); selection is part of the prefill and timed separately.
+    """
+    import torch
+    import synth
+    from sparse_draft_speculative_amd.toy_decoder import ToyDecoder
+
+    cfg = dict(synth.TOY_C5)
+    params = synth.toy_params(cfg, seed=seed, std=0.02)
+    vis, text = synth.toy_prompt(cfg, seed=seed)
+    n_vis = cfg["n_vis"]
+    prompt_len = n_vis + cfg["n_text"]
+    dec = ToyDecoder(params, prompt_len + n_new + max(gammas) + 2, dtype=torch.bfloat16)
+    first, q_text = dec.prefill(vis, text)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    idx = dec.select(q_text, prompt_len, 0, n_vis, cfg["topk"])
+    torch.cuda.synchronize()
+    sel_ms = (time.perf_counter() - t0) * 1e3
+    snap = dec.snapshot()
+
+    def timed(fn):
+        dec.restore(snap)
+        fn()                                   # warm-up pass
+        dec.restore(snap)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        res = fn()
+        torch.cuda.synchronize()
+        return res, time.perf_counter() - t
+
+    dense, t_dense = timed(lambda: dec.decode_dense(first, prompt_len, n_new))
+    out = {"workload": "toy decoder 4x512, 8/2/64 GQA, MLP 1536, vocab 8192, bf16, "
+                       f"prompt {n_vis} visual + {cfg['n_text']} text, K={cfg['topk']}, "
+                       f"{n_new} new tokens, weights N(0, 0.02^2)",
+           "selection_ms": round(sel_ms, 3),
+           "dense_only_tokens_per_s": round((n_new - 1) / t_dense, 2), "std": {}}
+    for g in gammas:
+        (toks, acc), t_std = timed(lambda: dec.decode_std(first, prompt_len, n_new, idx, 0,
+                                                           n_vis, g))
+        out["std"][f"gamma{g}"] = {
+            "tokens_per_s": round((n_new - 1) / t_std, 2),
+            "speedup_vs_dense": round(t_dense / t_std, 3),
+            "accepted_tokens_per_dense_step": round(float(np.mean([a + 1 for a in acc])), 3),
+            "alpha_hat": round(float(np.mean(acc)) / g, 4),
+            "cycles": len(acc),
+            "stream_equals_dense": toks == dense,
+        }
+    return out
+
+
+def cpu_baseline(cfg, cpu_layers, args, cycles_per_request):
     """The float64 oracle on the host, on a bounded sample of the workload.
 
-    Sample (layer 0): one dense verify pass (7 queries x 28 heads over 142k
-    keys), gamma sparse draft steps, one acceptance, and the selection scores
-    of one KV head over the first 64 text rows.  Per-request CPU time is
-    extrapolated: 28 layers x (selection scaled to 4 heads x 2,048 rows +
-    cycles x (draft + verify)) + cycles x accept.
+    Sample: for each of the first CPU_LAYERS layers, one dense verify pass
+    (7 queries x 28 heads over 142k keys), gamma sparse draft steps and the
+    selection scores of one KV head over CPU_ROWS text rows; plus one
+    acceptance.  Per-request CPU time is extrapolated to 28 layers x
+    (selection scaled to 4 heads x 2,048 rows + cycles x (draft + verify)) +
+    cycles x accept.
     """
-    import numpy as np
-    import torch
     import oracle
     import synth
 
     G = cfg.gamma
-    k = lay["k"].double().cpu().numpy()
-    v = lay["v"].double().cpu().numpy()
-    qv = lay["q_verify"].double().cpu().numpy()
-    qd = lay["q_draft"].double().cpu().numpy()
-    qt = lay["q_text"].double().cpu().numpy()
     gpg = cfg.n_q_heads // cfg.n_kv_heads
-    # a valid index set for the sparse steps: the planted runs are unknown
-    # here, so take every 34th visual position (K of them)
+    rows = CPU_ROWS
+    # a valid index set for the sparse steps: every (vis_len // K)-th visual
+    # position (the planted runs are not needed for timing)
     idx = np.tile(np.arange(cfg.topk) * (cfg.vis_len // cfg.topk), (cfg.n_kv_heads, 1))
-    t0 = time.perf_counter()
-    oracle.dense_verify(qv, k, v, cfg.verify_len)
-    t_verify = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    for j in range(G):
-        oracle.sparse_decode(qd[j], k, v, cfg.draft_len(j), cfg.vis_start, cfg.vis_len, idx)
-    t_draft = time.perf_counter() - t0
-    draft, logits = synth.accept_case(G, 152064, args.alpha, seed=1000, dtype=torch.float32)
+    t_verify = t_draft = t_sel = 0.0
+    for lay in cpu_layers:
+        k = lay["k"].double().numpy()
+        v = lay["v"].double().numpy()
+        qv = lay["q_verify"].double().numpy()
+        qd = lay["q_draft"].double().numpy()
+        qt = lay["q_text"].double().numpy()
+        t0 = time.perf_counter()
+        oracle.dense_verify(qv, k, v, cfg.verify_len)
+        t_verify += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for j in range(G):
+            oracle.sparse_decode(qd[j], k, v, cfg.draft_len(j), cfg.vis_start, cfg.vis_len, idx)
+        t_draft += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.selection_scores(qt[:gpg, :rows], k[:1], cfg.text_start, cfg.vis_start,
+                                cfg.vis_len)
+        t_sel += time.perf_counter() - t0
+    n = len(cpu_layers)
+    draft, logits = synth.accept_case(G, 152064, args.alpha, seed=1000)
     t0 = time.perf_counter()
     oracle.accept(draft.numpy(), logits.double().numpy())
     t_accept = time.perf_counter() - t0
-    rows = 64
-    t0 = time.perf_counter()
-    oracle.selection_scores(qt[:gpg, :rows], k[:1], cfg.text_start, cfg.vis_start, cfg.vis_len)
-    t_sel = time.perf_counter() - t0
-    sel_layer = t_sel * cfg.n_kv_heads * (cfg.n_text / rows)
-    per_req = (cfg.n_layers * (sel_layer + cycles_per_request * (t_draft + t_verify))
+    sel_layer = (t_sel / n) * cfg.n_kv_heads * (cfg.n_text / rows)
+    per_req = (cfg.n_layers * (sel_layer + cycles_per_request * (t_draft + t_verify) / n)
                + cycles_per_request * t_accept)
     try:
         from threadpoolctl import threadpool_info
@@ -323,11 +394,11 @@ def cpu_baseline(cfg, lay, args, cycles_per_request):
         "value": round(args.new_tokens / per_req, 4), "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"layer 0 of c4: dense verify (7x28 rows, 142k keys) {t_verify:.2f}s, "
-                   f"{G} sparse steps {t_draft:.2f}s, accept {t_accept:.3f}s, selection of "
-                   f"1 KV head x {rows} text rows {t_sel:.2f}s; extrapolated to 28 layers x "
-                   f"{cycles_per_request:.1f} cycles/request + full selection (x"
-                   f"{cfg.n_kv_heads * cfg.n_text // rows} rows*heads)"),
+        "sample": (f"layers 0-{n - 1} of the workload: dense verify (7x28 rows, 142k keys) "
+                   f"{t_verify:.2f}s, {G} sparse steps per layer {t_draft:.2f}s, selection of "
+                   f"1 KV head x {rows} text rows per layer {t_sel:.2f}s, one acceptance "
+                   f"{t_accept:.3f}s; extrapolated to 28 layers x {cycles_per_request:.1f} "
+                   f"cycles/request + full selection (4 KV heads x {cfg.n_text} rows)"),
         "sample_seconds": round(t_verify + t_draft + t_accept + t_sel, 2),
     }
 
