@@ -24,7 +24,6 @@ namespace stdspec {
 namespace {
 
 constexpr int kLseChunk = 8192;     // keys per workgroup in step 1 (MFMA)
-constexpr int kRowsPerLseWg = 128;  // text rows per workgroup in step 1
 constexpr int kColsPerScoreWg = 256;  // visual keys per workgroup in step 2
 constexpr int kXcds = 8;
 
@@ -67,72 +66,227 @@ __device__ __forceinline__ void tile_store(const u32x4_t (&r)[KPT], uint16_t* ld
 
 // ---------------------------------------------------------------------------
 // Step 1 (bf16, MFMA): partial (max, sum) of each text row over one key chunk.
-// Work item = (KV head, key chunk, 128-row block); 4 waves x 32 rows.  Keys
-// are staged in LDS (64 per tile, double buffered, the next tiles' loads in
-// flight in two register buffers) and are the M side of S^T = K Q^T, rows
-// the N side.  Each lane keeps its own running (max, fp64 sum) over the keys
-// it sees; the max moves only when a score exceeds it by 2^8 (exact: it is
-// only the shift of the exponent), and the four lanes of a column are merged
-// once at the end.  Only tiles that reach the causal (text) part or the
-// chunk end are masked.
+//
+// Work item = (KV head, key chunk, 128-row block).  Keys move global -> LDS
+// in 64-key tiles by direct-to-LDS loads (three buffers, two tiles in
+// flight).  Wave w takes key half w & 1 (32 keys) of every tile against row
+// half w >> 1 (64 rows), whose Q operands stay in registers, so every key
+// fragment read from LDS feeds four MFMA column blocks.  Scores are
+// S^T = K Q^T (keys on the M side).  Each lane keeps a running (max, sum)
+// per row over the keys it sees; the max moves only when a score exceeds it
+// by 2^8 (exact: it only shifts the exponent).  Sums run in fp32 within
+// three tiles and in fp64 across them.  Lane groups and the two key halves
+// are merged once at the end.  Only tiles that reach the causal (text) part
+// or the chunk end are masked.
+constexpr int kLseNB = 4;                      // 16-row column blocks per wave
+constexpr int kLseRows = 32 * kLseNB;          // text rows per workgroup (two row halves)
+constexpr int kLseKB = 2;                      // 16-key blocks per wave and tile
+static_assert(kLseKB == 2, "the tile sum below adds 4 * kLseKB = 8 terms");
+
+// s_waitcnt immediate waiting until at most n vector-memory operations are
+// outstanding (gfx9 encoding; expcnt and lgkmcnt left free).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Issue the direct-to-LDS loads of one 64-key tile.  Thread tid's u-th
+// 16-byte slot is s = 256u + tid (each wave instruction fills 64
+// consecutive slots); the slot's row and physical chunk give the logical
+// chunk through the K swizzle, and rows past the end re-read the last key.
 template <int D>
-__device__ __forceinline__ void lse_tile(const uint16_t* Ks, const bf16x8_t (*qb)[D / 32],
-                                         int t0, int key1, int text_start, const int* rpos,
-                                         float c, int col, int grp, float* m, double* l) {
-  constexpr int KST = D / 32;
-  floatx4_t sacc[4][2];
+__device__ __forceinline__ void lse_issue_tile(uint16_t* buf, const uint16_t* kh, int t0,
+                                               int last, int tid, int wave) {
+  constexpr int CPR = D / 8;
+  constexpr int LPT = 64 * CPR / 256;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    u32x4_t a[KST];
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk)
-      a[kk] = *reinterpret_cast<const u32x4_t*>(Ks + Tile<D>::off_k(kb * 16 + col, KST * grp + kk));
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kk]), qb[nb][kk], acc);
-      sacc[kb][nb] = acc;
-    }
-  }
-  const bool masked = t0 + 64 > text_start || t0 + 64 > key1;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = sacc[j >> 2][nb][j & 3];
-    if (masked) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = t0 + (j >> 2) * 16 + 4 * grp + (j & 3);
-        if (!(key < key1 && key <= rpos[nb])) v[j] = -INFINITY;
-      }
-    }
-    float tmax = v[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, v[j]);
-    if (tmax == -INFINITY) continue;
-    const float ts = tmax * c;                       // c > 0: max then scale
-    if (ts > m[nb] + 8.f) {
-      if (m[nb] != -INFINITY) l[nb] *= exp2((double)m[nb] - (double)ts);
-      m[nb] = ts;
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ps += fast_exp2(fmaf(v[j], c, -m[nb]));
-    l[nb] += (double)ps;
+  for (int u = 0; u < LPT; ++u) {
+    const int slot = 256 * u + tid;
+    const int row = slot / CPR, phys = slot % CPR;
+    const int logical = phys ^ (row % CPR);
+    const uint16_t* src = kh + (size_t)min(t0 + row, last) * D + logical * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + (256 * u + 64 * wave) * 8), 16, 0,
+                                     0);
   }
 }
 
+struct LseState {
+  float m[kLseNB];      // running max (base-2 units) per row block
+  float l32[kLseNB];    // sum relative to m since the last flush
+  double l[kLseNB];     // flushed sum relative to m
+};
+
+// Slow path for one row block, taken by the whole wave (MFMA operands and
+// results cover every lane, so no MFMA may sit under a lane-dependent
+// branch): lanes with need set take the max of their scores, move m when it
+// exceeds m + 8 and recompute the tile sum; other lanes keep ``fast``.
+// Written with selects only.
+template <int N>
+__device__ __forceinline__ float lse_rescue(const float (&v)[N], float c, LseState& st, int nb,
+                                            float fast) {
+  const bool need = !(fast <= 256.f);
+  float tmax = v[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) tmax = fmaxf(tmax, v[i]);
+  const float ts = tmax * c;                     // c > 0: max then scale
+  const bool move = need && tmax != -INFINITY && ts > st.m[nb] + 8.f;
+  const bool had = st.m[nb] != -INFINITY;
+  const double scale = exp2((double)(had ? st.m[nb] : ts) - (double)ts);
+  const double lnew = (st.l[nb] + (double)st.l32[nb]) * scale;
+  st.l[nb] = move ? lnew : st.l[nb];
+  st.l32[nb] = move ? 0.f : st.l32[nb];
+  st.m[nb] = move ? ts : st.m[nb];
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) t += fast_exp2(fmaf(v[i], c, -st.m[nb]));
+  t = tmax == -INFINITY ? 0.f : t;
+  return need ? t : fast;
+}
+
+// Where a tile reaches the chunk end or the causal part, the scores of keys
+// past key1 or after the row's own position are -inf.  Row rho of the
+// block is text row rho % n_text (the G heads' rows are stacked).
+struct LseMask {
+  int key1, R, n_text, text_start;
+  __device__ __forceinline__ void apply(float (&v)[4 * kLseKB], int rho, int key_base) const {
+    const int rpos = text_start + (rho < R ? rho % n_text : 0);
+#pragma unroll
+    for (int j = 0; j < 4 * kLseKB; ++j) {
+      const int key = key_base + (j >> 2) * 16 + (j & 3);
+      if (!(key < key1 && key <= rpos)) v[j] = -INFINITY;
+    }
+  }
+};
+
+// The wave's key fragments of one tile (kLseKB x KST 16-byte reads at the
+// byte addresses ``addr`` plus the buffer offset OFF).  The reads sit in one
+// asm block that also waits for them: the compiler, which cannot tell the
+// three buffers apart, would otherwise wait for every direct-to-LDS load in
+// flight (including the ones filling other buffers) before any LDS read.
+template <int OFF>
+__device__ __forceinline__ void lse_frag_read(u32x4_t (&a)[8], const uint32_t (&addr)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%16\n\t"
+      "ds_read_b128 %1, %9 offset:%16\n\t"
+      "ds_read_b128 %2, %10 offset:%16\n\t"
+      "ds_read_b128 %3, %11 offset:%16\n\t"
+      "ds_read_b128 %4, %12 offset:%16\n\t"
+      "ds_read_b128 %5, %13 offset:%16\n\t"
+      "ds_read_b128 %6, %14 offset:%16\n\t"
+      "ds_read_b128 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]),
+        "v"(addr[6]), "v"(addr[7]), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lse_frag_read(u32x4_t (&a)[4], const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF));
+}
+
+// One wave's share of one tile: key blocks 2*kh, 2*kh+1 of the tile in LDS
+// buffer OFF against the wave's kLseNB row blocks.  The scores of a row
+// block live only until their exps are taken; the rare slow path recomputes
+// them.
+template <int D, int OFF, bool MASK>
+__device__ __forceinline__ void lse_step(const uint32_t (&addr)[kLseKB * D / 32],
+                                         const bf16x8_t (*qb)[D / 32], int t0, const LseMask& mk,
+                                         int row0, float c, int grp, int col, int kh,
+                                         LseState& st) {
+  constexpr int KST = D / 32;
+  u32x4_t af[kLseKB * KST];
+  lse_frag_read<OFF>(af, addr);
+  u32x4_t a[kLseKB][KST];
+#pragma unroll
+  for (int kb = 0; kb < kLseKB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) a[kb][kk] = af[kb * KST + kk];
+  const int key_base = t0 + kLseKB * kh * 16 + 4 * grp;
+  float tot[kLseNB];
+#pragma unroll
+  for (int nb = 0; nb < kLseNB; ++nb) {
+    float v[4 * kLseKB];
+#pragma unroll
+    for (int kb = 0; kb < kLseKB; ++kb) {
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kb][kk]), qb[nb][kk], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * kb + i] = acc[i];
+    }
+    if constexpr (MASK) mk.apply(v, row0 + nb * 16 + col, key_base);
+    float p[4 * kLseKB];
+#pragma unroll
+    for (int j = 0; j < 4 * kLseKB; ++j) p[j] = fast_exp2(fmaf(v[j], c, -st.m[nb]));
+    // pairwise sum of the 8 terms
+    tot[nb] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  }
+  // every term <= 2^8 keeps the running-max invariant; NaN (an unset max
+  // against a masked score) and overflow fail the test and take the slow path
+  bool ok = true;
+#pragma unroll
+  for (int nb = 0; nb < kLseNB; ++nb) ok = ok && (tot[nb] <= 256.f);
+  if (__any(!ok)) {                    // wave-uniform: the MFMAs below run on every lane
+#pragma unroll
+    for (int nb = 0; nb < kLseNB; ++nb) {
+      float v[4 * kLseKB];
+#pragma unroll
+      for (int kb = 0; kb < kLseKB; ++kb) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kb][kk]), qb[nb][kk], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * kb + i] = acc[i];
+      }
+      if constexpr (MASK) mk.apply(v, row0 + nb * 16 + col, key_base);
+      tot[nb] = lse_rescue(v, c, st, nb, tot[nb]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < kLseNB; ++nb) st.l32[nb] += tot[nb];
+}
+
+__device__ __forceinline__ void lse_flush(LseState& st) {
+#pragma unroll
+  for (int nb = 0; nb < kLseNB; ++nb) {
+    st.l[nb] += (double)st.l32[nb];
+    st.l32[nb] = 0.f;
+  }
+}
+
+template <int D, int OFF>
+__device__ __forceinline__ void lse_tile(const uint32_t (&addr)[kLseKB * D / 32],
+                                         const bf16x8_t (*qb)[D / 32], int t0, const LseMask& mk,
+                                         int row0, float c, int grp, int col, int kh,
+                                         LseState& st) {
+  if (t0 + 64 <= mk.text_start && t0 + 64 <= mk.key1)
+    lse_step<D, OFF, false>(addr, qb, t0, mk, row0, c, grp, col, kh, st);
+  else
+    lse_step<D, OFF, true>(addr, qb, t0, mk, row0, c, grp, col, kh, st);
+}
+
+constexpr int kLseOcc = 2;                     // workgroups per CU
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void lse_partial_mfma(const uint16_t* __restrict__ qt,
+__global__ __launch_bounds__(256, kLseOcc) void lse_partial_mfma(const uint16_t* __restrict__ qt,
                                                            const uint16_t* __restrict__ k, Geo geo,
                                                            int n_chunks, int n_rb,
                                                            float* __restrict__ m_part,
                                                            double* __restrict__ l_part) {
-  constexpr int KST = D / 32, CPR = D / 8, KPT = 64 * CPR / 256;
-  __shared__ __align__(16) uint16_t Ks0[64 * D];
-  __shared__ __align__(16) uint16_t Ks1[64 * D];
+  constexpr int KST = D / 32;
+  constexpr int LPT = 64 * (D / 8) / 256;      // direct-to-LDS loads per thread per tile
+  constexpr int TB = 64 * D * 2;                // bytes of one tile buffer
+  __shared__ __align__(16) uint16_t Kbuf[3 * 64 * D];
+  uint16_t* Kb0 = Kbuf;
+  uint16_t* Kb1 = Kbuf + 64 * D;
+  uint16_t* Kb2 = Kbuf + 2 * 64 * D;
   const int n_items = geo.hkv * n_chunks * n_rb;
   const int item = xcd_item(blockIdx.x, n_items);
   if (item >= n_items) return;
@@ -142,72 +296,108 @@ __global__ __launch_bounds__(256, 2) void lse_partial_mfma(const uint16_t* __res
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const int kh = wave & 1, rh = wave >> 1;     // key half, row half
   const int R = geo.G * geo.n_text;
   const int n_keys = geo.text_start + geo.n_text;
   const int key0 = ch * kLseChunk, key1 = min(n_keys, key0 + kLseChunk);
+  const int row0 = rb * kLseRows + rh * (kLseRows / 2);   // first row of the wave
 
-  bf16x8_t qb[2][KST];
-  int rpos[2];
-  bool rok[2];
+  bf16x8_t qb[kLseNB][KST];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int rho = rb * kRowsPerLseWg + wave * 32 + nb * 16 + col;
-    rok[nb] = rho < R;
-    rpos[nb] = geo.text_start + (rok[nb] ? rho % geo.n_text : 0);
-    const uint16_t* qrow = qt + ((size_t)g * R + (rok[nb] ? rho : 0)) * D + (D / 4) * grp;
+  for (int nb = 0; nb < kLseNB; ++nb) {
+    const int rho = row0 + nb * 16 + col;
+    const bool ok = rho < R;
+    const uint16_t* qrow = qt + ((size_t)g * R + (ok ? rho : 0)) * D + (D / 4) * grp;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (rok[nb]) u = *reinterpret_cast<const uint4*>(qrow + 8 * kk);
+      if (ok) u = *reinterpret_cast<const uint4*>(qrow + 8 * kk);
       qb[nb][kk] = as_bf16x8(u);
     }
   }
-  float m[2] = {-INFINITY, -INFINITY};
-  double l[2] = {0.0, 0.0};
+  LseState st;
+#pragma unroll
+  for (int nb = 0; nb < kLseNB; ++nb) {
+    st.m[nb] = -INFINITY;
+    st.l32[nb] = 0.f;
+    st.l[nb] = 0.0;
+  }
 
-  const uint16_t* kh = k + (size_t)g * geo.capacity * D;
-  int rrow[KPT], rslot[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int cl = tid + 256 * u;
-    rrow[u] = cl / CPR;
-    rslot[u] = cl % CPR;
-  }
+  const uint16_t* khp = k + (size_t)g * geo.capacity * D;
   const int ntiles = (key1 - key0 + 63) / 64;
-  u32x4_t ra[KPT], rb_[KPT];
-  tile_load<D, KPT>(ra, kh, key0, key1 - 1, rrow, rslot);
-  tile_store<D, KPT>(ra, Ks0, rrow, rslot);
-  tile_load<D, KPT>(ra, kh, key0 + 64, key1 - 1, rrow, rslot);
-  tile_load<D, KPT>(rb_, kh, key0 + 128, key1 - 1, rrow, rslot);
-  for (int t = 0; t < ntiles; t += 2) {
-    __syncthreads();
-    tile_store<D, KPT>(ra, Ks1, rrow, rslot);
-    tile_load<D, KPT>(ra, kh, key0 + (t + 3) * 64, key1 - 1, rrow, rslot);
-    lse_tile<D>(Ks0, qb, key0 + t * 64, key1, geo.text_start, rpos, geo.c, col, grp, m, l);
-    __syncthreads();
-    tile_store<D, KPT>(rb_, Ks0, rrow, rslot);
-    tile_load<D, KPT>(rb_, kh, key0 + (t + 4) * 64, key1 - 1, rrow, rslot);
-    if (t + 1 < ntiles)
-      lse_tile<D>(Ks1, qb, key0 + (t + 1) * 64, key1, geo.text_start, rpos, geo.c, col, grp, m,
-                  l);
-  }
-  // merge the four lanes of each column, then write this chunk's partial
+  const int last = key1 - 1;
+  const LseMask mk{key1, R, geo.n_text, geo.text_start};
+  const float c = geo.c;
+  // LDS byte addresses of the wave's key fragments in buffer 0
+  uint32_t addr[kLseKB * KST];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float mm = max_over_groups(m[nb]);
-    double ll = (m[nb] == -INFINITY) ? 0.0 : l[nb] * exp2((double)m[nb] - (double)mm);
+  for (int kb = 0; kb < kLseKB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      addr[kb * KST + kk] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          Kbuf + Tile<D>::off_k((kLseKB * kh + kb) * 16 + col, KST * grp + kk)));
+  // Three LDS buffers, unrolled by three so every buffer is static.  Step t
+  // waits for its own tile (one newer tile may stay in flight), then after
+  // the barrier refills the buffer read in step t-1 with tile t+2.  Loads
+  // past the last tile re-read valid rows, so the count of loads in flight
+  // is the same at every step.
+  lse_issue_tile<D>(Kb0, khp, key0, last, tid, wave);
+  lse_issue_tile<D>(Kb1, khp, key0 + 64, last, tid, wave);
+  for (int t = 0; t < ntiles; t += 3) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+    __syncthreads();
+    lse_issue_tile<D>(Kb2, khp, key0 + (t + 2) * 64, last, tid, wave);
+    lse_tile<D, 0>(addr, qb, key0 + t * 64, mk, row0, c, grp, col, kh, st);
+    if (t + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      __syncthreads();
+      lse_issue_tile<D>(Kb0, khp, key0 + (t + 3) * 64, last, tid, wave);
+      lse_tile<D, TB>(addr, qb, key0 + (t + 1) * 64, mk, row0, c, grp, col, kh, st);
+    }
+    if (t + 2 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      __syncthreads();
+      lse_issue_tile<D>(Kb1, khp, key0 + (t + 4) * 64, last, tid, wave);
+      lse_tile<D, 2 * TB>(addr, qb, key0 + (t + 2) * 64, mk, row0, c, grp, col, kh, st);
+    }
+    lse_flush(st);
+  }
+  // no direct-to-LDS load may still be writing when the buffers are reused
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // merge the four lane groups of each row, then the two key halves via LDS
+  constexpr int HALF = kLseRows / 2;
+  float* xm = reinterpret_cast<float*>(Kb0);                      // [4 waves][HALF rows]
+  double* xl = reinterpret_cast<double*>(Kb1);                    // [4 waves][HALF rows]
+#pragma unroll
+  for (int nb = 0; nb < kLseNB; ++nb) {
+    const float mm = max_over_groups(st.m[nb]);
+    double ll = (st.m[nb] == -INFINITY) ? 0.0 : st.l[nb] * exp2((double)st.m[nb] - (double)mm);
     ll += __shfl_xor(ll, 16, kWave);
     ll += __shfl_xor(ll, 32, kWave);
-    const int rho = rb * kRowsPerLseWg + wave * 32 + nb * 16 + col;
-    if (grp == 0 && rok[nb]) {
+    if (grp == 0) {
+      xm[wave * HALF + nb * 16 + col] = mm;
+      xl[wave * HALF + nb * 16 + col] = ll;
+    }
+  }
+  __syncthreads();
+  if (tid < kLseRows) {
+    const int r = tid % HALF, w0 = 2 * (tid / HALF);   // the row half's two waves
+    const int rho = rb * kLseRows + tid;
+    const float m0 = xm[w0 * HALF + r], m1 = xm[(w0 + 1) * HALF + r];
+    const float M = fmaxf(m0, m1);
+    double L = 0.0;
+    if (m0 != -INFINITY) L += xl[w0 * HALF + r] * exp2((double)m0 - (double)M);
+    if (m1 != -INFINITY) L += xl[(w0 + 1) * HALF + r] * exp2((double)m1 - (double)M);
+    if (rho < R) {
       const size_t slot = (size_t)ch * geo.hq * geo.n_text + (size_t)g * R + rho;
-      m_part[slot] = mm;
-      l_part[slot] = ll;
+      m_part[slot] = M;
+      l_part[slot] = L;
     }
   }
 }
 
-// Step 1 merge: lse2 = M + log2(sum_c l_c 2^(m_c - M)), one thread per row.
 __global__ void lse_finalize(const float* __restrict__ m_part, const double* __restrict__ l_part,
                              int n_chunks, int rows, float* __restrict__ lse2) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
@@ -517,7 +707,7 @@ hipError_t launch_mfma_select(const SelectArgs& a, const Geo& geo, float* lse2, 
     const int n_keys = a.text_start + a.n_text;
     const int n_chunks = (n_keys + kLseChunk - 1) / kLseChunk;
     const int R = geo.G * a.n_text;
-    const int n_rb = (R + kRowsPerLseWg - 1) / kRowsPerLseWg;
+    const int n_rb = (R + kLseRows - 1) / kLseRows;
     const int n_items = a.hkv * n_chunks * n_rb;
     const int grid = ((n_items + kXcds - 1) / kXcds) * kXcds;
     lse_partial_mfma<D><<<grid, 256, 0, st>>>(qt, k, geo, n_chunks, n_rb, m_part, l_part);
