@@ -150,265 +150,239 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, bool ok, in
   }
 }
 
-// Move one 64-row tile of K and V: global -> registers (rows clamped to
-// the last valid one, key1 - 1, so every load is in bounds and the data past
-// the end is finite; it is masked out of the softmax) and registers -> LDS
-// (swizzled chunk slots).
-template <int D, int KPT>
-__device__ __forceinline__ void stage_load(u32x4_t (&kr)[KPT], u32x4_t (&vr)[KPT],
-                                           const uint16_t* kh, const uint16_t* vh, int t0,
-                                           int key1, const int (&rrow)[KPT],
-                                           const int (&rslot)[KPT]) {
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const size_t base = (size_t)min(t0 + rrow[u], key1 - 1) * D;
-    kr[u] = *reinterpret_cast<const u32x4_t*>(kh + base + (Tile<D>::slot_k(rrow[u], rslot[u]) << 3));
-    vr[u] = *reinterpret_cast<const u32x4_t*>(vh + base + (Tile<D>::slot_v(rrow[u], rslot[u]) << 3));
-  }
-}
-
-template <int D, int KPT>
-__device__ __forceinline__ void stage_store(const u32x4_t (&kr)[KPT], const u32x4_t (&vr)[KPT],
-                                            uint16_t* ks, uint16_t* vs, const int (&rrow)[KPT],
-                                            const int (&rslot)[KPT]) {
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    *reinterpret_cast<u32x4_t*>(ks + rrow[u] * D + (rslot[u] << 3)) = kr[u];
-    *reinterpret_cast<u32x4_t*>(vs + rrow[u] * D + (rslot[u] << 3)) = vr[u];
-  }
-}
-
-// Dense verify, one wave's share of a 64-key tile: the 32 keys of key half
-// kh (key blocks 2kh, 2kh+1) against the wave's two 16-column query blocks.
-// Half the keys per wave halves the LDS operand traffic compared with every
-// wave reading the whole tile.
-template <int D>
-struct HalfTile {
-  static constexpr int KST = D / 32;
-  static constexpr int DB = D / 16;
-
-  static __device__ __forceinline__ void run(const uint16_t* Ks, const uint16_t* Vs,
-                                             const bf16x8_t (*qb)[D / 32], int nblocks, int kh,
-                                             int t0, int len, int safe_end, const int* qpos,
-                                             float c, int col, int grp, float* m, float* lsum,
-                                             floatx4_t (*oacc)[D / 16]) {
-    // S^T for the two key blocks and the active query blocks
-    floatx4_t sacc[2][2];
-#pragma unroll
-    for (int kbi = 0; kbi < 2; ++kbi) {
-      const int row = (2 * kh + kbi) * 16 + col;
-      uint4 a[KST];
-#pragma unroll
-      for (int kk = 0; kk < KST; ++kk)
-        a[kk] = *reinterpret_cast<const uint4*>(Ks + Tile<D>::off_k(row, KST * grp + kk));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (nb < nblocks) {
-#pragma unroll
-          for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kk]), qb[nb][kk], acc);
-        }
-        sacc[kbi][nb] = acc;
-      }
-    }
-    float p[2][8];
-    const bool interior = t0 + 64 <= safe_end;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (nb >= nblocks) break;
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float sv = sacc[j >> 2][nb][j & 3] * c;
-        if (interior) {
-          x[j] = sv;
-        } else {
-          const int key = t0 + (2 * kh + (j >> 2)) * 16 + 4 * grp + (j & 3);
-          x[j] = (key < len && key <= qpos[nb]) ? sv : -INFINITY;
-        }
-      }
-      float tmax = x[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
-      tmax = max_over_groups(tmax);
-      if (tmax > m[nb] + kLazyMax) {     // rare: see online_update
-        const float alpha = fast_exp2(m[nb] - tmax);
-        lsum[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[nb][db] *= alpha;
-        m[nb] = tmax;
-      }
-      const float msafe = (m[nb] == -INFINITY) ? 0.f : m[nb];
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[nb][j] = fast_exp2(x[j] - msafe);
-        ps += p[nb][j];
-      }
-      lsum[nb] += ps;
-    }
-    // O^T += V^T P^T over the 32 keys (one MFMA step); the V^T operand is
-    // shared by both query blocks.
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      uint4 pw;
-      pw.x = pack_bf16x2(p[nb][0], p[nb][1]);
-      pw.y = pack_bf16x2(p[nb][2], p[nb][3]);
-      pw.z = pack_bf16x2(p[nb][4], p[nb][5]);
-      pw.w = pack_bf16x2(p[nb][6], p[nb][7]);
-      pb[nb] = as_bf16x8(pw);
-    }
-    const int r4 = col >> 2, rc = col & 3;
-    const int row0 = 32 * kh + 4 * grp + r4;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int chunk = 2 * db + (rc >> 1);
-      const int e = 4 * (rc & 1);
-      const uint2 lo = lds_read_tr16(Vs + Tile<D>::off_v(row0, chunk) + e);
-      const uint2 hi = lds_read_tr16(Vs + Tile<D>::off_v(row0 + 16, chunk) + e);
-      const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        if (nb < nblocks) oacc[nb][db] = mfma_bf16(va, pb[nb], oacc[nb][db]);
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
-// Dense verify: grid (split, KV head, 64-row block), 256 threads.
+// Dense verify: grid (split, KV head, 64-row block), 512 threads = 8 waves,
+// one workgroup per CU.
 //
 // The len keys form ceil(len/64) tiles of 64; split s takes tiles s,
 // s + S, s + 2S, ... (S splits, a function of len and H_kv only), so at any
 // moment the workgroups of a head sweep one contiguous region of the cache.
-// Waves: wave w reduces key half (w & 1) of every tile for query columns
-// 32*(w >> 1) .. +31 of the row block; the two key halves are merged in LDS
-// at the end.
-//
-// Pipeline per tile (one barrier per tile): tile i+1 moves from registers
-// into the other LDS buffer while tile i is reduced.  Loads and stores are
-// unconditional (indices past the end re-read the last row), so the number
-// of loads in flight is the same on every path and the compiler waits only
-// for the buffer it is about to store.
+// K and V tiles move global -> LDS by direct-to-LDS copies (no staging
+// registers) into four buffers, three tiles in flight.  Wave w reduces key
+// half w & 1 of every tile for the 16 query rows of block w >> 1; the two
+// key halves are merged in LDS at the end.  Every K/V byte is read from HBM
+// once per call when n_q * G <= 64.
+constexpr int kDenseThreads = 512;
+constexpr int kDenseBufs = 4;
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (gfx9 encoding; expcnt and lgkmcnt left free).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+// One direct-to-LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base is wave-uniform).  Issued from inline assembly
+// so the compiler, which cannot tell which LDS buffer such a copy fills and
+// would hold every later LDS read until all copies in flight had landed,
+// leaves the ordering to the kernel's explicit vmcnt waits and barriers.
+// M0 (the copy's LDS base) is saved and restored around it; one wait state
+// separates the M0 write from the copy.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %2\n\t"
+               "s_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Copy one 64-key tile of K and V (rows past the end re-read row len - 1)
+// into the swizzled LDS layout of Tile<D>.  Thread tid fills 16-byte slots
+// 512u + tid of each tensor; a slot's row and physical chunk give the
+// logical chunk by the (self-inverse) XOR swizzle.
 template <int D>
-__global__ __launch_bounds__(256, 2) void dense_mfma_kernel(
+__device__ __forceinline__ void dense_issue_tile(uint16_t* ks, uint16_t* vs, const uint16_t* kh,
+                                                 const uint16_t* vh, int t0, int len, int tid,
+                                                 int wave) {
+  constexpr int CPR = D / 8;
+  constexpr int LPT = 64 * CPR / kDenseThreads;
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int slot = kDenseThreads * u + tid;
+    const int row = slot / CPR, phys = slot % CPR;
+    const size_t base = (size_t)min(t0 + row, len - 1) * D;
+    const uint32_t dst = (kDenseThreads * u + 64 * wave) * 16;
+    dma16(kh + base + (Tile<D>::slot_k(row, phys) << 3), lds_addr(ks) + dst);
+    dma16(vh + base + (Tile<D>::slot_v(row, phys) << 3), lds_addr(vs) + dst);
+  }
+}
+
+// One wave's share of a 64-key tile: the 32 keys of key half kh (key
+// blocks 2kh, 2kh+1) against the wave's 16 query rows.
+template <int D>
+__device__ __forceinline__ void dense_step(const uint16_t* Ks, const uint16_t* Vs,
+                                           const bf16x8_t* qb, int kh, int t0, int len,
+                                           int safe_end, int qpos, float c, int col, int grp,
+                                           float& m, float& lsum, floatx4_t* oacc) {
+  constexpr int KST = D / 32;
+  constexpr int DB = D / 16;
+  floatx4_t sacc[2];
+#pragma unroll
+  for (int kbi = 0; kbi < 2; ++kbi) {
+    const int row = (2 * kh + kbi) * 16 + col;
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      const uint4 a = *reinterpret_cast<const uint4*>(Ks + Tile<D>::off_k(row, KST * grp + kk));
+      acc = mfma_bf16(as_bf16x8(a), qb[kk], acc);
+    }
+    sacc[kbi] = acc;
+  }
+  float x[8];
+  const bool interior = t0 + 64 <= safe_end;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float sv = sacc[j >> 2][j & 3] * c;
+    if (interior) {
+      x[j] = sv;
+    } else {
+      const int key = t0 + (2 * kh + (j >> 2)) * 16 + 4 * grp + (j & 3);
+      x[j] = (key < len && key <= qpos) ? sv : -INFINITY;
+    }
+  }
+  float tmax = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
+  tmax = max_over_groups(tmax);
+  if (tmax > m + kLazyMax) {              // rare: see online_update
+    const float alpha = fast_exp2(m - tmax);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    m = tmax;
+  }
+  const float msafe = (m == -INFINITY) ? 0.f : m;
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[j] - msafe);
+  lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  // O^T += V^T P^T over the 32 keys (one MFMA step per 16 output columns)
+  uint4 pw;
+  pw.x = pack_bf16x2(p[0], p[1]);
+  pw.y = pack_bf16x2(p[2], p[3]);
+  pw.z = pack_bf16x2(p[4], p[5]);
+  pw.w = pack_bf16x2(p[6], p[7]);
+  const bf16x8_t pb = as_bf16x8(pw);
+  const int r4 = col >> 2, rc = col & 3;
+  const int row0 = 32 * kh + 4 * grp + r4;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int chunk = 2 * db + (rc >> 1);
+    const int e = 4 * (rc & 1);
+    const uint2 lo = lds_read_tr16(Vs + Tile<D>::off_v(row0, chunk) + e);
+    const uint2 hi = lds_read_tr16(Vs + Tile<D>::off_v(row0 + 16, chunk) + e);
+    oacc[db] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, oacc[db]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, int len, int n_q, float c,
     int splits, float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
   constexpr int DB = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int KPT = 64 * CPR / 256;   // 16-byte chunks per thread per tensor
-  constexpr int TILE = 64 * D;          // elements of one K or V tile
-  __shared__ __align__(16) uint16_t smem[4 * TILE];   // K[2], V[2]; reused for the merge
-  uint16_t* Ks0 = smem;
-  uint16_t* Ks1 = smem + TILE;
-  uint16_t* Vs0 = smem + 2 * TILE;
-  uint16_t* Vs1 = smem + 3 * TILE;
+  constexpr int TILE = 64 * D;                       // elements of one K or V tile
+  constexpr int LPT = 64 * CPR / kDenseThreads;      // copies per thread per tensor per tile
+  __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE];   // [buffer][K, V]
 
   const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kh = wave & 1, qh = wave >> 1;
+  const int kh = wave & 1, nbw = wave >> 1;
   const int G = hq / hkv;
   const int Rg = n_q * G;
   const int col = lane & 15, grp = lane >> 4;
-  const int cbase = rb * 64 + qh * 32;                 // first query row of this wave
-  const int nblocks = Rg - cbase <= 0 ? 0 : (Rg - cbase > 16 ? 2 : 1);
-  int qi[2], hh[2], qpos[2];
-  bool rok[2];
-  bf16x8_t qb[2][D / 32];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int rho = cbase + nb * 16 + col;
-    rok[nb] = rho < Rg;
-    qi[nb] = rok[nb] ? rho / G : 0;
-    hh[nb] = g * G + (rok[nb] ? rho % G : 0);
-    qpos[nb] = len - n_q + qi[nb];
-    load_q_operand<D>(q + ((size_t)qi[nb] * hq + hh[nb]) * D, rok[nb], grp, qb[nb]);
-  }
+  const int r0 = rb * 64 + nbw * 16;                 // first query row of this wave
+  const bool active = r0 < Rg;                       // wave-uniform
+  const int rho = r0 + col;
+  const bool rok = rho < Rg;
+  const int qi = rok ? rho / G : 0;
+  const int hh = g * G + (rok ? rho % G : 0);
+  const int qpos = len - n_q + qi;
+  bf16x8_t qb[D / 32];
+  load_q_operand<D>(q + ((size_t)qi * hq + hh) * D, rok, grp, qb);
+  // the query operand has landed before any copy is in flight, so the
+  // compiler's own waits never count the copies
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   const int ntiles_all = (len + 63) / 64;
   const int ntiles = (ntiles_all - s + splits - 1) / splits;   // tiles of this split
   const int safe_end = len - n_q + 1;    // keys < safe_end: visible to every row
-  const uint16_t* kh_ = k + (size_t)g * capacity * D;
-  const uint16_t* vh_ = v + (size_t)g * capacity * D;
+  const uint16_t* khd = k + (size_t)g * capacity * D;
+  const uint16_t* vhd = v + (size_t)g * capacity * D;
   auto tile_key = [&](int i) { return (s + i * splits) * 64; };
+  auto kbuf = [&](int b) { return smem + b * 2 * TILE; };
+  auto vbuf = [&](int b) { return smem + b * 2 * TILE + TILE; };
 
-  int rrow[KPT], rslot[KPT];
+  float m = -INFINITY, lsum = 0.f;
+  floatx4_t oacc[DB];
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int cl = tid + 256 * u;
-    rrow[u] = cl / CPR;
-    rslot[u] = cl % CPR;
+  for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Step i: wait until tile i has landed (tiles i+1, i+2 may still be in
+  // flight), barrier, refill the buffer read in step i-1 with tile i+3,
+  // reduce tile i.  Copies past the last tile re-read valid rows, so the
+  // count in flight is the same at every step.  Unrolled by four so every
+  // buffer index is static.
+  constexpr int kInFlight = 2 * (kDenseBufs - 2) * LPT;   // copies of two tiles
+#pragma unroll
+  for (int b = 0; b < kDenseBufs - 1; ++b)
+    dense_issue_tile<D>(kbuf(b), vbuf(b), khd, vhd, tile_key(b), len, tid, wave);
+  for (int i = 0; i < ntiles; i += kDenseBufs) {
+#pragma unroll
+    for (int b = 0; b < kDenseBufs; ++b) {
+      if (i + b < ntiles) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInFlight));
+        __syncthreads();
+        const int nb = (b + kDenseBufs - 1) % kDenseBufs;
+        dense_issue_tile<D>(kbuf(nb), vbuf(nb), khd, vhd, tile_key(i + b + kDenseBufs - 1), len,
+                            tid, wave);
+        if (active)
+          dense_step<D>(kbuf(b), vbuf(b), qb, kh, tile_key(i + b), len, safe_end, qpos, c, col,
+                        grp, m, lsum, oacc);
+      }
+    }
   }
-
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  floatx4_t oacc[2][DB];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[nb][db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Two register buffers: a buffer is refilled right after its contents
-  // are written to LDS, so tiles i+2 and i+3 are in flight while tile i is
-  // reduced.  Unrolled by two so the buffers stay static.
-  u32x4_t ka[KPT], va[KPT], kb_[KPT], vb[KPT];
-  stage_load<D, KPT>(ka, va, kh_, vh_, tile_key(0), len, rrow, rslot);
-  stage_store<D, KPT>(ka, va, Ks0, Vs0, rrow, rslot);
-  stage_load<D, KPT>(ka, va, kh_, vh_, tile_key(1), len, rrow, rslot);
-  stage_load<D, KPT>(kb_, vb, kh_, vh_, tile_key(2), len, rrow, rslot);
-  for (int i = 0; i < ntiles; i += 2) {
-    __syncthreads();
-    stage_store<D, KPT>(ka, va, Ks1, Vs1, rrow, rslot);
-    stage_load<D, KPT>(ka, va, kh_, vh_, tile_key(i + 3), len, rrow, rslot);
-    if (nblocks)
-      HalfTile<D>::run(Ks0, Vs0, qb, nblocks, kh, tile_key(i), len, safe_end, qpos, c, col, grp,
-                       m, lsum, oacc);
-    __syncthreads();
-    stage_store<D, KPT>(kb_, vb, Ks0, Vs0, rrow, rslot);
-    stage_load<D, KPT>(kb_, vb, kh_, vh_, tile_key(i + 4), len, rrow, rslot);
-    if (nblocks && i + 1 < ntiles)
-      HalfTile<D>::run(Ks1, Vs1, qb, nblocks, kh, tile_key(i + 1), len, safe_end, qpos, c, col,
-                       grp, m, lsum, oacc);
-  }
+  // every copy has landed before the buffers are reused for the merge
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
 
   // merge the two key halves: odd waves hand (m, l, O) to their even partner
-  constexpr int XS = 2 * (2 + 4 * DB);                 // floats per lane
+  constexpr int XS = 2 + 4 * DB;                     // floats per lane
   float* xch = reinterpret_cast<float*>(smem);
-  __syncthreads();
-  if (kh == 1 && nblocks) {
-    float* dst = xch + (size_t)(qh * 64 + lane) * XS;
+  if (kh == 1 && active) {
+    float* dst = xch + (size_t)(nbw * 64 + lane) * XS;
+    dst[0] = m;
+    dst[1] = lsum;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      dst[nb * (2 + 4 * DB) + 0] = m[nb];
-      dst[nb * (2 + 4 * DB) + 1] = lsum[nb];
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[nb * (2 + 4 * DB) + 2 + 4 * db + i] = oacc[nb][db][i];
-    }
+      for (int i = 0; i < 4; ++i) dst[2 + 4 * db + i] = oacc[db][i];
   }
   __syncthreads();
-  if (kh == 1 || !nblocks) return;
-  const float* src = xch + (size_t)(qh * 64 + lane) * XS;
+  if (kh == 1 || !active) return;
+  const float* src = xch + (size_t)(nbw * 64 + lane) * XS;
+  const float m1 = src[0];
+  const float l1 = src[1];
+  const float M = fmaxf(m, m1);
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+  const float a0 = fast_exp2(m - Ms), a1 = fast_exp2(m1 - Ms);
+  const float L = sum_over_groups(lsum * a0 + l1 * a1);
+  if (!rok) return;
+  const size_t slot = (size_t)s * rows_total + (size_t)qi * hq + hh;
+  if (grp == 0) ml[slot] = make_float2(M, L);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    if (nb >= nblocks) break;
-    const float m1 = src[nb * (2 + 4 * DB) + 0];
-    const float l1 = src[nb * (2 + 4 * DB) + 1];
-    const float M = fmaxf(m[nb], m1);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    const float a0 = fast_exp2(m[nb] - Ms), a1 = fast_exp2(m1 - Ms);
-    const float L = sum_over_groups(lsum[nb] * a0 + l1 * a1);
-    if (!rok[nb]) continue;
-    const size_t slot = (size_t)s * rows_total + (size_t)qi[nb] * hq + hh[nb];
-    if (grp == 0) ml[slot] = make_float2(M, L);
+  for (int db = 0; db < DB; ++db) {
+    floatx4_t r;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      floatx4_t r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = oacc[nb][db][i] * a0 + src[nb * (2 + 4 * DB) + 2 + 4 * db + i] * a1;
-      *reinterpret_cast<floatx4_t*>(o + slot * D + db * 16 + 4 * grp) = r;
-    }
+    for (int i = 0; i < 4; ++i) r[i] = oacc[db][i] * a0 + src[2 + 4 * db + i] * a1;
+    *reinterpret_cast<floatx4_t*>(o + slot * D + db * 16 + 4 * grp) = r;
   }
 }
 
@@ -629,10 +603,12 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 // Split combine: out[r] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // M = max_s m_s.  One 256-thread workgroup per query row.  Thread (sg, dq)
 // merges splits sg, sg + NSG, ... online (running max, rescale on a new
-// max), reading each split's (m, l) together with its float4 of outputs in
-// the same round of loads; the NSG groups are then merged in LDS in a fixed
-// order, so the result does not depend on timing.
+// max); the loads of kCombineBatch of its splits are issued together
+// before any is merged, so a call waits about one memory latency per batch.
+// The NSG groups are then merged in LDS in a fixed order, so the result
+// does not depend on timing.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 8;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
@@ -646,19 +622,31 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int dq = tid % DQ, sg = tid / DQ;
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int s = sg; s < splits; s += NSG) {
-    const float2 st = ml[(size_t)s * rows + r];
-    const float4 x = *reinterpret_cast<const float4*>(o + ((size_t)s * rows + r) * D + 4 * dq);
-    const float Mn = fmaxf(M, st.x);
-    const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
-    const float a = fast_exp2(M - Ms), b = fast_exp2(st.x - Ms);
-    L = L * a + st.y * b;
-    acc.x = acc.x * a + x.x * b;
-    acc.y = acc.y * a + x.y * b;
-    acc.z = acc.z * a + x.z * b;
-    acc.w = acc.w * a + x.w * b;
-    M = Mn;
+  for (int s0 = sg; s0 < splits; s0 += NSG * kCombineBatch) {
+    float2 st[kCombineBatch];
+    float4 x[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int s = s0 + u * NSG;
+      st[u] = make_float2(-INFINITY, 0.f);
+      x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < splits) {
+        st[u] = ml[(size_t)s * rows + r];
+        x[u] = *reinterpret_cast<const float4*>(o + ((size_t)s * rows + r) * D + 4 * dq);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float Mn = fmaxf(M, st[u].x);
+      const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+      const float a = fast_exp2(M - Ms), b = fast_exp2(st[u].x - Ms);
+      L = L * a + st[u].y * b;
+      acc.x = acc.x * a + x[u].x * b;
+      acc.y = acc.y * a + x[u].y * b;
+      acc.z = acc.z * a + x[u].z * b;
+      acc.w = acc.w * a + x[u].w * b;
+      M = Mn;
+    }
   }
   part[sg][dq] = acc;
   stat[sg][dq] = make_float2(M, L);
@@ -727,7 +715,7 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   } else {
     const int rows_group = a.n_q * (a.hq / a.hkv);
     dim3 grid(a.splits, a.hkv, (rows_group + 63) / 64);
-    dense_mfma_kernel<D><<<grid, 256, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, a.len, a.n_q,
+    dense_mfma_kernel<D><<<grid, kDenseThreads, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, a.len, a.n_q,
                                                c, a.splits, reinterpret_cast<float2*>(a.ml), a.o,
                                                a.n_q * a.hq);
   }

@@ -22,10 +22,10 @@ inline int pow2_floor(long long x) {
 // S takes tiles s, s+S, s+2S, ...  S depends only on (len, n_kv_heads),
 // never on n_q, so a query row sees the same splits and the same reduction
 // order whatever the number of rows in the call.  S is sized so one layer
-// launches about 512 workgroups: two resident per CU on 256 CUs, one round.
+// launches about 256 workgroups: one resident per CU on 256 CUs, one round.
 inline int dense_split_count(int len, int n_kv_heads) {
   const int tiles = (len + 63) / 64;
-  const int target = n_kv_heads >= 512 ? 1 : 512 / n_kv_heads;
+  const int target = n_kv_heads >= 256 ? 1 : 256 / n_kv_heads;
   return tiles < target ? tiles : target;
 }
 
