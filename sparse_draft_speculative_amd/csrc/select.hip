@@ -603,63 +603,94 @@ __global__ __launch_bounds__(64) void colscore_valu(const T* __restrict__ qt,
 // order then emits every score > T plus the lowest-positioned copies of T.
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkBatch = 8;      // loads issued together per thread
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) red[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    int w = lane < kTopkThreads / 64 ? red[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(w, o, kWave);
-      if (lane >= o) w += y;
-    }
-    if (lane < kTopkThreads / 64) red[lane] = w;  // inclusive wave prefix
-  }
-  __syncthreads();
-  total = red[kTopkThreads / 64 - 1];
-  const int before = wave > 0 ? red[wave - 1] : 0;
-  __syncthreads();
-  return before + x - v;
-}
-
+// Step 3: one 1024-thread workgroup per KV head.
+//  * Radix select on the order-preserving bits of the (non-negative fp32)
+//    scores, four 8-bit digits from the top: each pass histograms the digit
+//    of the elements that match the prefix so far and keeps the digit that
+//    contains the K-th largest.  Each wave counts into its own LDS
+//    histogram, and since scores of one head share their top bits, a thread
+//    adds runs of equal digits as one atomic.
+//  * Stable compaction: wave w owns a contiguous range of positions; it
+//    counts the elements above the threshold T and the copies of T, a block
+//    scan turns the counts into output offsets (copies of T go to the lowest
+//    positions first), and the wave writes its range in 64-element chunks
+//    with a ballot prefix, so idx comes out in ascending position order.
 __global__ __launch_bounds__(kTopkThreads) void radix_topk(const float* __restrict__ scores,
                                                            int vis_len, int vis_start, int topk,
                                                            int32_t* __restrict__ idx_out) {
+  __shared__ unsigned whist[kTopkWaves][256];   // per-wave digit histograms
   __shared__ unsigned hist[256];
-  __shared__ int red[kTopkThreads / 64];
+  __shared__ int wcount[2][kTopkWaves];
   __shared__ unsigned sh_prefix;
   __shared__ int sh_remaining;
   const int g = blockIdx.x;
   const unsigned* bits = reinterpret_cast<const unsigned*>(scores + (size_t)g * vis_len);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   unsigned prefix = 0, pmask = 0;
   int remaining = topk;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 256; b += kTopkThreads) hist[b] = 0;
+    unsigned* wh = whist[wave];
+    for (int b = lane; b < 256; b += 64) wh[b] = 0;
     __syncthreads();
-    for (int j = tid; j < vis_len; j += kTopkThreads) {
-      const unsigned b = bits[j];
-      if ((b & pmask) == prefix) atomicAdd(&hist[(b >> shift) & 255u], 1u);
+    unsigned run_digit = 0, run_len = 0;
+    for (int j0 = tid; j0 < vis_len; j0 += kTopkBatch * kTopkThreads) {
+      // a batch of clamped loads first, so their latencies overlap
+      unsigned v[kTopkBatch];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u)
+        v[u] = bits[min(j0 + u * kTopkThreads, vis_len - 1)];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        if (j0 + u * kTopkThreads < vis_len && (v[u] & pmask) == prefix) {
+          const unsigned d = (v[u] >> shift) & 255u;
+          if (d != run_digit && run_len) {
+            atomicAdd(&wh[run_digit], run_len);
+            run_len = 0;
+          }
+          run_digit = d;
+          ++run_len;
+        }
+      }
+    }
+    if (run_len) atomicAdd(&wh[run_digit], run_len);
+    __syncthreads();
+    if (tid < 256) {
+      unsigned t = 0;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) t += whist[w][tid];
+      hist[tid] = t;
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, dgt = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + (int)hist[b] >= remaining) { dgt = b; break; }
-        cum += hist[b];
+    if (tid < 64) {
+      // the digit holding the remaining-th largest: lane l sums bins
+      // 255-4l .. 252-4l, a wave suffix scan orders them from the top
+      unsigned c4 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c4 += hist[255 - 4 * lane - i];
+      unsigned incl = c4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
       }
-      sh_prefix = prefix | ((unsigned)dgt << shift);
-      sh_remaining = remaining - cum;
+      const unsigned excl = incl - c4;
+      const bool here = excl < (unsigned)remaining && incl >= (unsigned)remaining;
+      if (here) {
+        unsigned cum = excl;
+        int dgt = 255 - 4 * lane;
+        for (int i = 0; i < 4; ++i) {
+          const unsigned h = hist[255 - 4 * lane - i];
+          if (cum + h >= (unsigned)remaining) { dgt = 255 - 4 * lane - i; break; }
+          cum += h;
+        }
+        sh_prefix = prefix | ((unsigned)dgt << shift);
+        sh_remaining = remaining - (int)cum;
+      }
     }
     __syncthreads();
     prefix = sh_prefix;
@@ -670,26 +701,54 @@ __global__ __launch_bounds__(kTopkThreads) void radix_topk(const float* __restri
   const unsigned T = prefix;
   const int need_eq = remaining;  // copies of T to keep, >= 1
 
-  // stable compaction over contiguous per-thread segments
-  const int per = (vis_len + kTopkThreads - 1) / kTopkThreads;
-  const int j0 = min(vis_len, tid * per), j1 = min(vis_len, j0 + per);
+  // per-wave counts over contiguous ranges of whole 64-element chunks
+  const int chunks = (vis_len + 63) / 64;
+  const int per_wave = (chunks + kTopkWaves - 1) / kTopkWaves;
+  const int c0 = wave * per_wave, c1 = min(chunks, c0 + per_wave);
   int n_gt = 0, n_eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const unsigned b = bits[j];
-    n_gt += b > T;
-    n_eq += b == T;
+  for (int cb = c0; cb < c1; cb += kTopkBatch) {
+    unsigned v[kTopkBatch];
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) v[u] = bits[min((cb + u) * 64 + lane, vis_len - 1)];
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) {
+      const bool valid = cb + u < c1 && (cb + u) * 64 + lane < vis_len;
+      n_gt += __popcll(__ballot(valid && v[u] > T));
+      n_eq += __popcll(__ballot(valid && v[u] == T));
+    }
   }
-  int tot;
-  const int eq_before = block_exclusive_scan(n_eq, red, tot);
-  const int take_eq = max(0, min(n_eq, need_eq - eq_before));
-  const int off = block_exclusive_scan(n_gt + take_eq, red, tot);
-  int32_t* dst = idx_out + (size_t)g * topk + off;
-  int w = 0, eq_used = 0;
-  for (int j = j0; j < j1; ++j) {
-    const unsigned b = bits[j];
-    const bool take = b > T || (b == T && eq_used < take_eq);
-    eq_used += b == T;
-    if (take) dst[w++] = vis_start + j;
+  if (lane == 0) {
+    wcount[0][wave] = n_gt;
+    wcount[1][wave] = n_eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += wcount[0][w];
+    eq_before += wcount[1][w];
+  }
+  // copies of T taken before this wave's range, and by it
+  const int eq_take_before = min(eq_before, need_eq);
+  int out = gt_before + eq_take_before;
+  int eq_seen = eq_before;
+  const unsigned long long lower = (1ull << lane) - 1ull;
+  for (int cb = c0; cb < c1; cb += kTopkBatch) {
+    unsigned v[kTopkBatch];
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) v[u] = bits[min((cb + u) * 64 + lane, vis_len - 1)];
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) {
+      const int j = (cb + u) * 64 + lane;
+      const bool valid = cb + u < c1 && j < vis_len;
+      const bool is_eq = valid && v[u] == T;
+      const unsigned long long eq_mask = __ballot(is_eq);
+      const int eq_rank = eq_seen + __popcll(eq_mask & lower);   // copies of T before j
+      const bool take = (valid && v[u] > T) || (is_eq && eq_rank < need_eq);
+      const unsigned long long take_mask = __ballot(take);
+      if (take) idx_out[(size_t)g * topk + out + __popcll(take_mask & lower)] = vis_start + j;
+      out += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
   }
 }
 
