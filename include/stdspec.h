@@ -182,6 +182,32 @@ std_status_t std_dense_verify_attn(const std_attn_shape_t* shape, const void* q,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Device-resident length variants of (b) and (c).
+ *
+ * A draft-verify cycle changes the valid length after every acceptance
+ * (Methodology item 3: accepted tokens are appended); keeping that length in
+ * device memory lets a caller capture a whole cycle once (for example in a
+ * HIP graph) and replay it with no host round trip.  These calls read the
+ * valid length when their kernels run:
+ *     len = min(max(*len_dev + len_offset, 1), kv->len)
+ * kv->len is the upper bound: it sizes the launch and the workspace (query
+ * the *_workspace functions with it), and every other argument, check and
+ * result is that of the host-length call with this len.  The caller keeps
+ * len >= vis_start + vis_len (sparse) and len >= n_q (dense); outside that
+ * range the result is unspecified but every access stays inside the cache.
+ * len_dev is an int32 device pointer, e.g. the seq_len std_accept advances.
+ * ------------------------------------------------------------------------ */
+std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* shape, const void* q,
+                                         const std_kv_t* kv, const int32_t* len_dev,
+                                         int32_t len_offset, std_vis_t vis, const int32_t* idx,
+                                         int32_t topk, void* out, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* shape, const void* q,
+                                        int32_t n_q, const std_kv_t* kv, const int32_t* len_dev,
+                                        int32_t len_offset, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * (d) Greedy acceptance plus the bonus token.
  *
  * Technical summary, Methodology item 3: verification finds the longest

@@ -9,6 +9,10 @@ binding over it (torch supplies device memory and the HIP stream):
   std_dense_verify_attn   dense verify attention (gamma+1 queries, full KV)
   std_accept              greedy longest-prefix acceptance + bonus token
 
+std_sparse_decode_attn_dlen / std_dense_verify_attn_dlen read the valid
+cache length from device memory, so a whole draft-verify cycle can be
+captured once and replayed.
+
 Importing this package does not load the library; the first call does, and
 fails loudly if it has not been built.
 """
@@ -16,9 +20,9 @@ fails loudly if it has not been built.
 from ._lib import (  # noqa: F401
     StdError, load, attn_shape, kv_desc,
     std_select_topk, std_select_topk_workspace,
-    std_sparse_decode_attn, std_sparse_decode_workspace,
-    std_dense_verify_attn, std_dense_verify_workspace,
+    std_sparse_decode_attn, std_sparse_decode_workspace, std_sparse_decode_attn_dlen,
+    std_dense_verify_attn, std_dense_verify_workspace, std_dense_verify_attn_dlen,
     std_accept,
     PreparedCall, prepare_dense_verify, prepare_sparse_decode, prepare_select_topk,
-    prepare_accept,
+    prepare_accept, prepare_dense_verify_dlen, prepare_sparse_decode_dlen,
 )

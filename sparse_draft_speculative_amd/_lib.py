@@ -56,7 +56,12 @@ _SIGS = {
     "std_dense_verify_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, ctypes.POINTER(KV)]),
     "std_dense_verify_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I,
                                              ctypes.POINTER(KV), _P, _P, _SZ, _P]),
+    "std_dense_verify_attn_dlen": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I,
+                                                  ctypes.POINTER(KV), _P, _I, _P, _P, _SZ, _P]),
     "std_sparse_decode_workspace": (_SZ, [ctypes.POINTER(AttnShape), ctypes.POINTER(KV), Vis, _I]),
+    "std_sparse_decode_attn_dlen": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P,
+                                                   ctypes.POINTER(KV), _P, _I, Vis, _P, _I, _P,
+                                                   _P, _SZ, _P]),
     "std_sparse_decode_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, ctypes.POINTER(KV),
                                               Vis, _P, _I, _P, _P, _SZ, _P]),
     "std_select_topk_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, Vis, _I,
@@ -165,6 +170,30 @@ def std_dense_verify_attn(q, k, v, length, out=None, scale=None, workspace=None,
     return out
 
 
+def std_dense_verify_attn_dlen(q, k, v, max_len, len_dev, len_offset, out=None, scale=None,
+                               workspace=None, stream=None):
+    """Dense verify with the valid length read on the device:
+    min(max(len_dev[0] + len_offset, 1), max_len)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (len_dev, "len_dev")):
+        _dev(t, n)
+    if len_dev.dtype != torch.int32:
+        raise ValueError("len_dev must be int32")
+    n_q, hq, d = q.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, max_len)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    ws = _workspace(lib.std_dense_verify_workspace(ctypes.byref(shape), n_q, ctypes.byref(kv)),
+                    q.device, workspace)
+    _check(lib.std_dense_verify_attn_dlen(ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv),
+                                          _ptr(len_dev), int(len_offset), _ptr(out), _ptr(ws),
+                                          ws.numel(), _stream(stream)),
+           "std_dense_verify_attn_dlen")
+    return out
+
+
 def std_sparse_decode_workspace(shape, k, length, vis_start, vis_len, topk):
     return load().std_sparse_decode_workspace(ctypes.byref(shape),
                                               ctypes.byref(kv_desc(k, None, length)),
@@ -196,6 +225,35 @@ def std_sparse_decode_attn(q, k, v, length, vis_start, vis_len, idx, out=None, s
                                       _ptr(idx), topk, _ptr(out), _ptr(ws), ws.numel(),
                                       _stream(stream)),
            "std_sparse_decode_attn")
+    return out
+
+
+def std_sparse_decode_attn_dlen(q, k, v, max_len, len_dev, len_offset, vis_start, vis_len, idx,
+                                out=None, scale=None, workspace=None, stream=None):
+    """Sparse draft attention with the valid length read on the device:
+    min(max(len_dev[0] + len_offset, 1), max_len)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (len_dev, "len_dev")):
+        _dev(t, n)
+    if idx.dtype != torch.int32 or len_dev.dtype != torch.int32:
+        raise ValueError("idx and len_dev must be int32")
+    hq, d = q.shape
+    hkv = k.shape[0]
+    if idx.dim() != 2 or idx.shape[0] != hkv:
+        raise ValueError("idx must be [H_kv][K]")
+    topk = idx.shape[1]
+    shape = attn_shape(hq, hkv, d, scale)
+    kv = kv_desc(k, v, max_len)
+    vis = Vis(vis_start, vis_len)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    ws = _workspace(lib.std_sparse_decode_workspace(ctypes.byref(shape), ctypes.byref(kv), vis,
+                                                    topk), q.device, workspace)
+    _check(lib.std_sparse_decode_attn_dlen(ctypes.byref(shape), _ptr(q), ctypes.byref(kv),
+                                           _ptr(len_dev), int(len_offset), vis, _ptr(idx), topk,
+                                           _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "std_sparse_decode_attn_dlen")
     return out
 
 
@@ -302,6 +360,38 @@ def prepare_sparse_decode(q, k, v, vis_start, vis_len, idx, out, workspace, stre
             idx.shape[1], _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     return PreparedCall("std_sparse_decode_attn", args, kv,
                         (shape, kv, q, k, v, idx, out, workspace))
+
+
+def prepare_dense_verify_dlen(q, k, v, out, workspace, len_dev, len_offset, max_len=None,
+                              stream=None, scale=None):
+    """Prepared dense verify reading its length from len_dev (see
+    std_dense_verify_attn_dlen); max_len defaults to the cache capacity."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (workspace, "workspace"),
+                 (len_dev, "len_dev")):
+        _dev(t, n)
+    n_q, hq, d = q.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, k.shape[1] if max_len is None else max_len)
+    args = (ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv), _ptr(len_dev), int(len_offset),
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall("std_dense_verify_attn_dlen", args, kv,
+                        (shape, kv, q, k, v, out, workspace, len_dev))
+
+
+def prepare_sparse_decode_dlen(q, k, v, vis_start, vis_len, idx, out, workspace, len_dev,
+                               len_offset, max_len=None, stream=None, scale=None):
+    """Prepared sparse draft attention reading its length from len_dev."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (out, "out"),
+                 (workspace, "workspace"), (len_dev, "len_dev")):
+        _dev(t, n)
+    hq, d = q.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, k.shape[1] if max_len is None else max_len)
+    args = (ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(len_dev), int(len_offset),
+            Vis(vis_start, vis_len), _ptr(idx), idx.shape[1], _ptr(out), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    return PreparedCall("std_sparse_decode_attn_dlen", args, kv,
+                        (shape, kv, q, k, v, idx, out, workspace, len_dev))
 
 
 def prepare_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, idx_out,

@@ -140,9 +140,13 @@ size_t std_dense_verify_workspace(const std_attn_shape_t* s, int32_t n_q, const 
   return split_workspace(splits, n_q * s->n_q_heads, s->head_dim).bytes();
 }
 
-std_status_t std_dense_verify_attn(const std_attn_shape_t* s, const void* q, int32_t n_q,
-                                   const std_kv_t* kv, void* out, void* ws, size_t ws_bytes,
-                                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q,
+                          const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
+                          void* out, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_shape(s));
   TRY(check_kv(kv, true));
   TRY(check_extent(s, kv));
@@ -161,12 +165,31 @@ std_status_t std_dense_verify_attn(const std_attn_shape_t* s, const void* q, int
   a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
   a.capacity = kv->capacity; a.len = kv->len; a.n_q = n_q;
+  a.len_dev = len_dev; a.len_off = len_off;
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = false;
   a.ml = static_cast<float*>(ws);
   a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(w.ml_bytes));
   a.splits = splits; a.chunk = chunk;
   return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+std_status_t std_dense_verify_attn(const std_attn_shape_t* s, const void* q, int32_t n_q,
+                                   const std_kv_t* kv, void* out, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return dense_verify(s, q, n_q, kv, nullptr, 0, out, ws, ws_bytes, stream);
+}
+
+std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* s, const void* q, int32_t n_q,
+                                        const std_kv_t* kv, const int32_t* len_dev,
+                                        int32_t len_offset, void* out, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  CHECK(len_dev, STD_ERR_INVALID_ARGUMENT, "len_dev is null");
+  return dense_verify(s, q, n_q, kv, len_dev, len_offset, out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- sparse draft
@@ -178,9 +201,14 @@ size_t std_sparse_decode_workspace(const std_attn_shape_t* s, const std_kv_t* kv
   return split_workspace(sparse_splits(kv, vis, topk), s->n_q_heads, s->head_dim).bytes();
 }
 
-std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
-                                    std_vis_t vis, const int32_t* idx, int32_t topk, void* out,
-                                    void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
+                           const int32_t* len_dev, int32_t len_off, std_vis_t vis,
+                           const int32_t* idx, int32_t topk, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
   TRY(check_shape(s));
   TRY(check_kv(kv, true));
   TRY(check_extent(s, kv));
@@ -196,6 +224,7 @@ std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, co
   a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
   a.capacity = kv->capacity; a.len = kv->len; a.n_q = 1;
+  a.len_dev = len_dev; a.len_off = len_off;
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = true; a.idx = idx;
   a.vis_start = vis.vis_start; a.vis_len = vis.vis_len; a.topk = topk;
@@ -203,6 +232,25 @@ std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, co
   a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(w.ml_bytes));
   a.splits = splits; a.chunk = kSparseChunk;
   return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
+                                    std_vis_t vis, const int32_t* idx, int32_t topk, void* out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  return sparse_decode(s, q, kv, nullptr, 0, vis, idx, topk, out, ws, ws_bytes, stream);
+}
+
+std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* q,
+                                         const std_kv_t* kv, const int32_t* len_dev,
+                                         int32_t len_offset, std_vis_t vis, const int32_t* idx,
+                                         int32_t topk, void* out, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  CHECK(len_dev, STD_ERR_INVALID_ARGUMENT, "len_dev is null");
+  return sparse_decode(s, q, kv, len_dev, len_offset, vis, idx, topk, out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- selection

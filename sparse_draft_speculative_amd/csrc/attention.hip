@@ -46,6 +46,17 @@ struct KeyList {
   }
 };
 
+// Valid cache length of a call: the host value, or (device-length calls)
+// min(max(*dev + off, 1), max) read when the kernel runs, so a decode loop
+// captured once in a graph sees the length the previous step committed.
+struct LenSrc {
+  int max;
+  const int32_t* dev;
+  int off;
+  __device__ __forceinline__ int get() const { return dev ? min(max_(*dev + off, 1), max) : max; }
+  static __device__ __forceinline__ int max_(int a, int b) { return a > b ? a : b; }
+};
+
 // One tile of 16*NKB keys (NKB = 1, 2 or 4 key blocks) for one wave's 16
 // query columns.
 template <int D, int NKB>
@@ -284,11 +295,12 @@ __device__ __forceinline__ void dense_step(const uint16_t* Ks, const uint16_t* V
 template <int D>
 __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int hq, int hkv, int capacity, int len, int n_q, float c,
+    const uint16_t* __restrict__ v, int hq, int hkv, int capacity, LenSrc lsrc, int n_q, float c,
     int splits, float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
   constexpr int DB = D / 16;
   constexpr int CPR = D / 8;
   constexpr int TILE = 64 * D;                       // elements of one K or V tile
+  const int len = lsrc.get();
   constexpr int LPT = 64 * CPR / kDenseThreads;      // copies per thread per tensor per tile
   __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE];   // [buffer][K, V]
 
@@ -312,7 +324,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   const int ntiles_all = (len + 63) / 64;
-  const int ntiles = (ntiles_all - s + splits - 1) / splits;   // tiles of this split
+  // tiles of this split (none when a device length leaves it past the end)
+  const int ntiles = s < ntiles_all ? (ntiles_all - s + splits - 1) / splits : 0;
   const int safe_end = len - n_q + 1;    // keys < safe_end: visible to every row
   const uint16_t* khd = k + (size_t)g * capacity * D;
   const uint16_t* vhd = v + (size_t)g * capacity * D;
@@ -405,8 +418,9 @@ template <int D>
 __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
-    const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, int n_entries,
+    const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, LenSrc lsrc,
     int splits, float2* __restrict__ ml, float* __restrict__ o) {
+  const int n_entries = vis_start + topk + max(0, lsrc.get() - vis_end);
   constexpr int EW = kSparseEntriesPerWave;
   constexpr int NKB = EW / 16;
   using TM = TileMath<D, NKB>;
@@ -537,8 +551,11 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
 template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int hq, int hkv,
-    int capacity, int len, int n_q, float c, KeyList kl, int n_entries, int chunk,
+    int capacity, LenSrc lsrc, int n_q, float c, KeyList kl, int sparse_chunk,
     float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
+  const int len = lsrc.get();
+  const int n_entries = kl.sparse ? kl.vis_start + kl.topk + max(0, len - kl.vis_end) : len;
+  const int chunk = kl.sparse ? sparse_chunk : (n_entries + gridDim.z - 1) / gridDim.z;
   constexpr int DPL = D / 64;  // output elements per lane
   __shared__ float qs[D];
   __shared__ float ps[64];
@@ -690,14 +707,13 @@ hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D>
-hipError_t launch_valu(const AttnArgs& a, const KeyList& kl, int n_entries, hipStream_t st) {
+hipError_t launch_valu(const AttnArgs& a, const KeyList& kl, hipStream_t st) {
   const int rows_group = a.n_q * (a.hq / a.hkv);
   dim3 grid(rows_group, a.hkv, a.splits);
   attn_valu_kernel<T, D><<<grid, 64, 0, st>>>(
       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-      a.hq, a.hkv, a.capacity, a.len, a.n_q, a.scale * kLog2e, kl, n_entries,
-      a.sparse ? a.chunk : (n_entries + a.splits - 1) / a.splits,
-      reinterpret_cast<float2*>(a.ml), a.o, a.n_q * a.hq);
+      a.hq, a.hkv, a.capacity, LenSrc{a.len, a.len_dev, a.len_off}, a.n_q, a.scale * kLog2e, kl,
+      a.chunk, reinterpret_cast<float2*>(a.ml), a.o, a.n_q * a.hq);
   return hipGetLastError();
 }
 
@@ -707,17 +723,18 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const float c = a.scale * kLog2e;
+  const LenSrc lsrc{a.len, a.len_dev, a.len_off};
   if (a.sparse) {
-    const int n_entries = sparse_list_len(a.len, a.vis_start, a.vis_len, a.topk);
     sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv), 64 * kSparseWaves, 0, st>>>(
         q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
-        a.topk, n_entries, a.splits, reinterpret_cast<float2*>(a.ml), a.o);
+        a.topk, lsrc, a.splits, reinterpret_cast<float2*>(a.ml), a.o);
   } else {
     const int rows_group = a.n_q * (a.hq / a.hkv);
     dim3 grid(a.splits, a.hkv, (rows_group + 63) / 64);
-    dense_mfma_kernel<D><<<grid, kDenseThreads, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, a.len, a.n_q,
-                                               c, a.splits, reinterpret_cast<float2*>(a.ml), a.o,
-                                               a.n_q * a.hq);
+    dense_mfma_kernel<D><<<grid, kDenseThreads, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, lsrc,
+                                                         a.n_q, c, a.splits,
+                                                         reinterpret_cast<float2*>(a.ml), a.o,
+                                                         a.n_q * a.hq);
   }
   return hipGetLastError();
 }
@@ -732,14 +749,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     err = a.d == 128 ? launch_mfma<128>(a, st) : launch_mfma<64>(a, st);
   } else {
     KeyList kl{a.sparse, a.idx, a.vis_start, a.vis_start + a.vis_len, a.topk};
-    const int n_entries =
-        a.sparse ? sparse_list_len(a.len, a.vis_start, a.vis_len, a.topk) : a.len;
     if (a.bf16)
-      err = a.d == 128 ? launch_valu<uint16_t, 128>(a, kl, n_entries, st)
-                       : launch_valu<uint16_t, 64>(a, kl, n_entries, st);
+      err = a.d == 128 ? launch_valu<uint16_t, 128>(a, kl, st)
+                       : launch_valu<uint16_t, 64>(a, kl, st);
     else
-      err = a.d == 128 ? launch_valu<float, 128>(a, kl, n_entries, st)
-                       : launch_valu<float, 64>(a, kl, n_entries, st);
+      err = a.d == 128 ? launch_valu<float, 128>(a, kl, st)
+                       : launch_valu<float, 64>(a, kl, st);
   }
   if (err != hipSuccess) return err;
   return a.bf16 ? launch_combine<uint16_t>(a, st) : launch_combine<float>(a, st);

@@ -70,6 +70,9 @@ struct AttnArgs {
   int hq, hkv, d;
   float scale;
   int capacity, len, n_q;
+  // device-resident length (null: use len); valid length min(*len_dev + len_off, len)
+  const int32_t* len_dev;
+  int len_off;
   bool bf16;
   // sparse key list; for dense, sparse == false
   bool sparse;

@@ -101,6 +101,32 @@ def test_sparse_decode_rejects():
     assert call(topk=0, idx=0) == _lib.STD_ERR_WORKSPACE_TOO_SMALL   # K = 0 is legal
 
 
+def test_device_length_calls_reject():
+    """The device-length variants need len_dev and run the host checks of
+    their host-length twins (kv->len is the bound)."""
+    lib = _lib.load()
+    sh = _shape()
+    kv = _kv()
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    P = ctypes.c_void_p
+
+    def dense(len_dev=FAKE, n_q=6):
+        return lib.std_dense_verify_attn_dlen(ctypes.byref(sh), P(FAKE), n_q, ctypes.byref(kv),
+                                              P(len_dev), 0, P(FAKE), None, 0, None)
+
+    def sparse(len_dev=FAKE, topk=64):
+        return lib.std_sparse_decode_attn_dlen(ctypes.byref(sh), P(FAKE), ctypes.byref(kv),
+                                               P(len_dev), 1, _lib.Vis(0, 800), P(FAKE), topk,
+                                               P(FAKE), None, 0, None)
+
+    assert dense(len_dev=0) == E
+    assert dense(n_q=901) == E
+    assert dense() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert sparse(len_dev=0) == E
+    assert sparse(topk=801) == E
+    assert sparse() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_select_rejects():
     lib = _lib.load()
     sh = _shape()

@@ -1,0 +1,154 @@
+"""Device-resident length: the *_dlen calls against the oracle, and a whole
+draft-verify-accept cycle captured once in a HIP graph and replayed.
+
+The cycle follows the pages' decoding procedure (technical summary,
+Methodology item 3): gamma sparse draft steps at lengths t+1 .. t+gamma,
+one dense verify of gamma+1 queries at length t+gamma+1, then greedy
+acceptance, which advances the device length by n+1.  Each replay is
+checked against eager host-length calls at the length the replay saw, with
+eager work and synchronisations between replays.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_draft_speculative_amd as sd
+    sd.load()
+    return sd
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+@pytest.fixture(scope="module")
+def c2(lib):
+    cfg = synth.config("c2", extra=64)
+    lay = synth.attention_layer(cfg, 0, device="cuda")
+    idx_ref, _ = oracle.select_topk(f64(lay["q_text"]), f64(lay["k"]), cfg.text_start,
+                                    cfg.vis_start, cfg.vis_len, cfg.topk)
+    idx = torch.from_numpy(np.asarray(idx_ref, dtype=np.int32)).cuda()
+    return cfg, lay, idx, np.asarray(idx_ref)
+
+
+def test_dlen_calls_match_oracle(lib, c2):
+    cfg, lay, idx, idx_np = c2
+    kf, vf = f64(lay["k"]), f64(lay["v"])
+    cap = cfg.capacity
+    for t in (cfg.ctx, cfg.ctx + 17, cap - cfg.gamma - 1):
+        seq = torch.tensor([t], dtype=torch.int32, device="cuda")
+        q = lay["q_draft"][0].contiguous()
+        out = lib.std_sparse_decode_attn_dlen(q, lay["k"], lay["v"], cap, seq, 1, cfg.vis_start,
+                                              cfg.vis_len, idx)
+        qv = lay["q_verify"]
+        outv = lib.std_dense_verify_attn_dlen(qv, lay["k"], lay["v"], cap, seq, cfg.gamma + 1)
+        torch.cuda.synchronize()
+        ref = oracle.sparse_decode(f64(q), kf, vf, t + 1, cfg.vis_start, cfg.vis_len, idx_np)
+        refv = oracle.dense_verify(f64(qv), kf, vf, t + cfg.gamma + 1)
+        say(f"t={t}: sparse err {max_abs(f64(out), ref):.2e} dense err "
+            f"{max_abs(f64(outv), refv):.2e}")
+        assert max_abs(f64(out), ref) <= TOL
+        assert max_abs(f64(outv), refv) <= TOL
+
+
+def test_dlen_at_the_bound_equals_host_length(lib, c2):
+    """With the device length equal to the bound the launch is the host-length
+    launch: results are bitwise equal."""
+    cfg, lay, idx, _ = c2
+    L = cfg.verify_len
+    seq = torch.tensor([L], dtype=torch.int32, device="cuda")
+    a = lib.std_dense_verify_attn_dlen(lay["q_verify"], lay["k"], lay["v"], L, seq, 0)
+    b = lib.std_dense_verify_attn(lay["q_verify"], lay["k"], lay["v"], L)
+    q = lay["q_draft"][0].contiguous()
+    c = lib.std_sparse_decode_attn_dlen(q, lay["k"], lay["v"], L, seq, 0, cfg.vis_start,
+                                        cfg.vis_len, idx)
+    d = lib.std_sparse_decode_attn(q, lay["k"], lay["v"], L, cfg.vis_start, cfg.vis_len, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_graph_replayed_cycle(lib, c2):
+    cfg, lay, idx, _ = c2
+    G, cap = cfg.gamma, cfg.capacity
+    dev = torch.device("cuda")
+    shape = lib.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+    ws_s = torch.zeros(lib.std_sparse_decode_workspace(shape, lay["k"], cap, cfg.vis_start,
+                                                       cfg.vis_len, cfg.topk), dtype=torch.uint8,
+                       device=dev)
+    ws_d = torch.zeros(lib.std_dense_verify_workspace(shape, G + 1, lay["k"], cap),
+                       dtype=torch.uint8, device=dev)
+    seq = torch.tensor([cfg.ctx], dtype=torch.int32, device=dev)
+    q_draft = [lay["q_draft"][j].contiguous() for j in range(G)]
+    outs = [torch.empty_like(q_draft[0]) for _ in range(G)]
+    out_v = torch.empty_like(lay["q_verify"])
+    draft, logits = synth.accept_case(G, 4096, 0.7, seed=11)
+    draft, logits = draft.to(dev), logits.to(dev)
+    toks = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    n_out = torch.empty(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    calls = [lib.prepare_sparse_decode_dlen(q_draft[j], lay["k"], lay["v"], cfg.vis_start,
+                                            cfg.vis_len, idx, outs[j], ws_s, seq, 1 + j,
+                                            stream=stream)
+             for j in range(G)]
+    calls.append(lib.prepare_dense_verify_dlen(lay["q_verify"], lay["k"], lay["v"], out_v, ws_d,
+                                               seq, G + 1, stream=stream))
+
+    def cycle():
+        for c in calls:
+            c()
+        lib.std_accept(draft, logits, out_tokens=toks, n_out=n_out, seq_len=seq)
+
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        cycle()                                    # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    seq.fill_(cfg.ctx)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        cycle()
+    torch.cuda.synchronize()
+    seq.fill_(cfg.ctx)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        t = int(seq.item())
+        graph.replay()
+        torch.cuda.synchronize()
+        # eager reference at the length this replay saw
+        for j in range(G):
+            ref = lib.std_sparse_decode_attn(q_draft[j], lay["k"], lay["v"], t + 1 + j,
+                                             cfg.vis_start, cfg.vis_len, idx)
+            torch.cuda.synchronize()
+            assert max_abs(f64(outs[j]), f64(ref)) <= 1e-2, (rep, j)
+        refv = lib.std_dense_verify_attn(lay["q_verify"], lay["k"], lay["v"], t + G + 1)
+        torch.cuda.synchronize()
+        assert max_abs(f64(out_v), f64(refv)) <= 1e-2, rep
+        ref_toks, ref_n, _, _ = oracle.accept(draft.cpu().numpy(), f64(logits))
+        assert toks.cpu().numpy().tolist() == list(ref_toks)
+        assert int(n_out.item()) == ref_n
+        assert int(seq.item()) == t + ref_n, "the accept step advances the device length"
+        say(f"replay {rep}: t={t} -> {int(seq.item())}")
