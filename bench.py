@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--alpha", type=float, default=0.95)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense-tokens", type=int, default=8)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the calls one by one instead of replaying captured phases")
     ap.add_argument("--no-toy", action="store_true",
                     help="skip the end-to-end toy decoder measurement")
     return ap.parse_args()
@@ -122,28 +124,79 @@ def main():
     out_sp = torch.empty(cfg.n_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
     out_dv = torch.empty(G + 1, cfg.n_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
 
+    # Every call runs on one stream and reads the valid cache length from
+    # the device scalar `seq` (the position of the pending token x_t), which
+    # the acceptance step advances; so each phase is captured once as a HIP
+    # graph and replayed every cycle (--no-graph launches the same calls
+    # one by one instead).
+    st = torch.cuda.Stream()
+    seq = torch.zeros(1, dtype=torch.int32, device=dev)
     sel_calls = [sd.prepare_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
-                                        cfg.vis_start, cfg.vis_len, cfg.topk, idx[l], ws_sel)
+                                        cfg.vis_start, cfg.vis_len, cfg.topk, idx[l], ws_sel,
+                                        stream=st)
                  for l, lay in enumerate(layers)]
     q_draft = [[lay["q_draft"][j].contiguous() for j in range(G)] for lay in layers]
-    sp_calls = [[sd.prepare_sparse_decode(q_draft[l][j], lay["k"], lay["v"], cfg.vis_start,
-                                          cfg.vis_len, idx[l], out_sp, ws_sparse)
+    sp_calls = [[sd.prepare_sparse_decode_dlen(q_draft[l][j], lay["k"], lay["v"], cfg.vis_start,
+                                               cfg.vis_len, idx[l], out_sp, ws_sparse, seq, 1 + j,
+                                               max_len=max_len, stream=st)
                  for l, lay in enumerate(layers)] for j in range(G)]
-    dv_calls = [sd.prepare_dense_verify(lay["q_verify"], lay["k"], lay["v"], out_dv, ws_dense)
+    dv_calls = [sd.prepare_dense_verify_dlen(lay["q_verify"], lay["k"], lay["v"], out_dv,
+                                             ws_dense, seq, G + 1, max_len=max_len, stream=st)
                 for lay in layers]
     q_one = [lay["q_verify"][:1].contiguous() for lay in layers]
     out_one = torch.empty(1, cfg.n_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
-    dn_calls = [sd.prepare_dense_verify(q_one[l], lay["k"], lay["v"], out_one, ws_dense)
+    dn_calls = [sd.prepare_dense_verify_dlen(q_one[l], lay["k"], lay["v"], out_one, ws_dense,
+                                             seq, 1, max_len=max_len, stream=st)
                 for l, lay in enumerate(layers)]
 
     vocab = 152064
     pool = []
-    for s in range(16):
-        draft, logits = synth.accept_case(G, vocab, args.alpha, seed=1000 + s, dtype=torch.bfloat16)
+    for s_ in range(16):
+        draft, logits = synth.accept_case(G, vocab, args.alpha, seed=1000 + s_,
+                                          dtype=torch.bfloat16)
         pool.append((draft.to(dev), logits.to(dev)))
     toks = torch.empty(G + 1, dtype=torch.int32, device=dev)
     n_out = torch.zeros(1, dtype=torch.int32, device=dev)
-    acc_calls = [sd.prepare_accept(d_, lg, toks, n_out) for d_, lg in pool]
+    acc_calls = [sd.prepare_accept(d_, lg, toks, n_out, seq_len=seq, stream=st)
+                 for d_, lg in pool]
+
+    def draft_phase():
+        for j in range(G):
+            for l in range(L):
+                sp_calls[j][l]()
+
+    def verify_phase():
+        for c in dv_calls:
+            c()
+
+    def dense_token():
+        for c in dn_calls:
+            c()
+        seq.add_(1)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        seq.fill_(cfg.ctx)
+        draft_phase()                      # warm-up launches outside any capture
+        verify_phase()
+        dense_token()
+        for c in acc_calls:
+            c()
+    torch.cuda.synchronize()
+    if args.no_graph:
+        run_draft, run_verify, run_dense = draft_phase, verify_phase, dense_token
+        run_accept = acc_calls
+    else:
+        def capture(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                fn()
+            return g
+        g_draft, g_verify, g_dense = capture(draft_phase), capture(verify_phase), capture(dense_token)
+        g_acc = [capture(c) for c in acc_calls]
+        run_draft, run_verify, run_dense = g_draft.replay, g_verify.replay, g_dense.replay
+        run_accept = [g.replay for g in g_acc]
+        torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -151,39 +204,34 @@ def main():
         """One request; returns (new tokens, cycles, phase times ms or None)."""
         e_sel = (ev(), ev())
         cyc_ev = []
-        e_sel[0].record()
-        for c in sel_calls:
-            c()
-        e_sel[1].record()
-        t = cfg.ctx
-        produced = 1                       # the pending token x_t comes from prefill
-        cycles = 0
-        emitted = 0
-        sp_bytes = dv_bytes = 0
-        while produced < args.new_tokens:
-            es = (ev(), ev(), ev(), ev()) if timing else None
-            if es:
+        with torch.cuda.stream(st):
+            e_sel[0].record()
+            for c in sel_calls:
+                c()
+            e_sel[1].record()
+            seq.fill_(cfg.ctx)
+            t = cfg.ctx
+            produced = 1                   # the pending token x_t comes from prefill
+            cycles = 0
+            emitted = 0
+            sp_bytes = dv_bytes = 0
+            while produced < args.new_tokens:
+                es = (ev(), ev(), ev(), ev())
                 es[0].record()
-            for j in range(G):
-                for l in range(L):
-                    sp_calls[j][l](t + 1 + j)
-                sp_bytes += L * attn_bytes_sparse(cfg, t + 1 + j)
-            if es:
+                run_draft()
                 es[1].record()
-            for l in range(L):
-                dv_calls[l](t + G + 1)
-            dv_bytes += L * attn_bytes_dense(cfg, t + G + 1, G + 1)
-            if es:
+                run_verify()
                 es[2].record()
-            acc_calls[cycles % len(acc_calls)]()
-            if es:
+                run_accept[cycles % len(run_accept)]()
                 es[3].record()
                 cyc_ev.append(es)
-            n = int(n_out.item())          # host sync: advances the cache length
-            emitted += n
-            produced += n
-            t += n
-            cycles += 1
+                sp_bytes += sum(L * attn_bytes_sparse(cfg, t + 1 + j) for j in range(G))
+                dv_bytes += L * attn_bytes_dense(cfg, t + G + 1, G + 1)
+                n = int(n_out.item())      # host sync: only to count the tokens
+                emitted += n
+                produced += n
+                t += n
+                cycles += 1
         torch.cuda.synchronize()
         ph = None
         if timing:
@@ -208,11 +256,12 @@ def main():
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
     e0, e1 = ev(), ev()
-    e0.record()
-    for i in range(args.dense_tokens):
-        for c in dn_calls:
-            c(cfg.ctx + 1 + i)
-    e1.record()
+    with torch.cuda.stream(st):
+        seq.fill_(cfg.ctx)
+        e0.record()
+        for i in range(args.dense_tokens):
+            run_dense()
+        e1.record()
     torch.cuda.synchronize()
     dense_ms_per_tok = e0.elapsed_time(e1) / args.dense_tokens
     dense_gbps = L * attn_bytes_dense(cfg, cfg.ctx + 1, 1) / (dense_ms_per_tok * 1e-3) / 1e9

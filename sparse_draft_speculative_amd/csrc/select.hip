@@ -24,7 +24,8 @@ namespace stdspec {
 namespace {
 
 constexpr int kLseChunk = 8192;     // keys per workgroup in step 1 (MFMA)
-constexpr int kColsPerScoreWg = 256;  // visual keys per workgroup in step 2
+constexpr int kColKB = 4;            // 16-key blocks per wave in step 2
+constexpr int kColsPerScoreWg = 4 * 16 * kColKB;  // visual keys per workgroup in step 2
 constexpr int kXcds = 8;
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (each with its
@@ -445,12 +446,13 @@ __global__ __launch_bounds__(64) void lse_valu(const T* __restrict__ qt, const T
 }
 
 // ---------------------------------------------------------------------------
-// Step 2 (bf16, MFMA): column sums over all text rows of the group for 256
-// visual keys.  S = Q K^T with rows on the M side (streamed through LDS, 64
-// per tile, double buffered) and keys on the N side (4 blocks of 16 per
-// wave, held in registers).  Each lane owns one key per block and sums its
-// rows; partial sums of a tile are fp32 and are added into fp64
-// accumulators; the four lanes of a key are merged at the end in fp64.
+// Step 2 (bf16, MFMA): column sums over all text rows of the group for
+// kColsPerScoreWg visual keys.  S = Q K^T with rows on the M side (streamed
+// through LDS, 64 per tile, double buffered) and keys on the N side
+// (kColKB blocks of 16 per wave, held in registers).  Each lane owns one key
+// per block and sums its rows; partial sums of a tile are fp32 and are added
+// into fp64 accumulators; the four lanes of a key are merged at the end in
+// fp64.
 template <int D>
 __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restrict__ qt,
                                                         const uint16_t* __restrict__ k, Geo geo,
@@ -458,6 +460,7 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
                                                         float lse_factor, int n_ct,
                                                         float* __restrict__ scores) {
   constexpr int KST = D / 32, CPR = D / 8, KPT = 64 * CPR / 256;
+  constexpr int KB = kColKB;
   __shared__ __align__(16) uint16_t Qs0[64 * D];
   __shared__ __align__(16) uint16_t Qs1[64 * D];
   __shared__ float Ls[2][64];
@@ -471,17 +474,19 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
   const int R = geo.G * geo.n_text;
 
   // key operands: B[k = d][n = key], key = base + kb*16 + col (clamped)
-  bf16x8_t kbop[4][KST];
+  bf16x8_t kbop[KB][KST];
   const uint16_t* kh = k + (size_t)g * geo.capacity * D;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int j = min(ct * kColsPerScoreWg + wave * 64 + kb * 16 + col, geo.vis_len - 1);
+  for (int kb = 0; kb < KB; ++kb) {
+    const int j = min(ct * kColsPerScoreWg + wave * 16 * KB + kb * 16 + col, geo.vis_len - 1);
     const uint16_t* krow = kh + (size_t)(geo.vis_start + j) * D + (D / 4) * grp;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
       kbop[kb][kk] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(krow + 8 * kk));
   }
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  double acc[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) acc[kb] = 0.0;
 
   const uint16_t* qg = qt + (size_t)g * R * D;
   const float* lg = lse + (size_t)g * R;
@@ -498,7 +503,9 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
   // one 64-row tile: four 16-row blocks; a block's 16 MFMAs are issued
   // before the previous block's exponentials are summed
   auto tile = [&](const uint16_t* Qs, const float* L) {
-    float cs[4] = {0.f, 0.f, 0.f, 0.f};
+    float cs[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) cs[kb] = 0.f;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       u32x4_t a[KST];
@@ -508,21 +515,21 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
       float lrow[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) lrow[i] = L[qb * 16 + 4 * grp + i];
-      floatx4_t sv[4];
+      floatx4_t sv[KB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         floatx4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk) x = mfma_bf16(as_bf16x8(a[kk]), kbop[kb][kk], x);
         sv[kb] = x;
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs[kb] += fast_exp2(fmaf(sv[kb][i], geo.c, -lrow[i]));
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) acc[kb] += (double)cs[kb];
+    for (int kb = 0; kb < KB; ++kb) acc[kb] += (double)cs[kb];
   };
 
   const int ntiles = (R + 63) / 64;
@@ -548,11 +555,11 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
   }
   const double inv = 1.0 / ((double)geo.G * (double)geo.n_text);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     double a = acc[kb];
     a += __shfl_xor(a, 16, kWave);
     a += __shfl_xor(a, 32, kWave);
-    const int j = ct * kColsPerScoreWg + wave * 64 + kb * 16 + col;
+    const int j = ct * kColsPerScoreWg + wave * 16 * KB + kb * 16 + col;
     if (grp == 0 && j < geo.vis_len) scores[(size_t)g * geo.vis_len + j] = (float)(a * inv);
   }
 }
