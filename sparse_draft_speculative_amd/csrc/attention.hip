@@ -176,33 +176,6 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, bool ok, in
 constexpr int kDenseThreads = 512;
 constexpr int kDenseBufs = 4;
 
-// s_waitcnt immediate: at most n vector-memory operations outstanding
-// (gfx9 encoding; expcnt and lgkmcnt left free).
-constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
-
-// One direct-to-LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 l (lds_base is wave-uniform).  Issued from inline assembly
-// so the compiler, which cannot tell which LDS buffer such a copy fills and
-// would hold every later LDS read until all copies in flight had landed,
-// leaves the ordering to the kernel's explicit vmcnt waits and barriers.
-// M0 (the copy's LDS base) is saved and restored around it; one wait state
-// separates the M0 write from the copy.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\t"
-               "s_mov_b32 m0, %2\n\t"
-               "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %1, off\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
 // Copy one 64-key tile of K and V (rows past the end re-read row len - 1)
 // into the swizzled LDS layout of Tile<D>.  Thread tid fills 16-byte slots
 // 512u + tid of each tensor; a slot's row and physical chunk give the

@@ -24,8 +24,12 @@ namespace stdspec {
 namespace {
 
 constexpr int kLseChunk = 8192;     // keys per workgroup in step 1 (MFMA)
-constexpr int kColKB = 4;            // 16-key blocks per wave in step 2
-constexpr int kColsPerScoreWg = 4 * 16 * kColKB;  // visual keys per workgroup in step 2
+constexpr int kColKB = 3;            // 16-key blocks per wave in step 2
+constexpr int kColWaves = 8;         // waves per workgroup in step 2
+constexpr int kColOcc = 2;           // step-2 workgroups per CU
+constexpr int kColBufs = 4;          // LDS tile buffers in step 2 (a power of two)
+constexpr int kColThreads = 64 * kColWaves;
+constexpr int kColsPerScoreWg = kColWaves * 16 * kColKB;  // visual keys per workgroup in step 2
 constexpr int kXcds = 8;
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (each with its
@@ -83,10 +87,6 @@ constexpr int kLseNB = 4;                      // 16-row column blocks per wave
 constexpr int kLseRows = 32 * kLseNB;          // text rows per workgroup (two row halves)
 constexpr int kLseKB = 2;                      // 16-key blocks per wave and tile
 static_assert(kLseKB == 2, "the tile sum below adds 4 * kLseKB = 8 terms");
-
-// s_waitcnt immediate waiting until at most n vector-memory operations are
-// outstanding (gfx9 encoding; expcnt and lgkmcnt left free).
-constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -446,32 +446,59 @@ __global__ __launch_bounds__(64) void lse_valu(const T* __restrict__ qt, const T
 }
 
 // ---------------------------------------------------------------------------
-// Step 2 (bf16, MFMA): column sums over all text rows of the group for
-// kColsPerScoreWg visual keys.  S = Q K^T with rows on the M side (streamed
-// through LDS, 64 per tile, double buffered) and keys on the N side
-// (kColKB blocks of 16 per wave, held in registers).  Each lane owns one key
-// per block and sums its rows; partial sums of a tile are fp32 and are added
-// into fp64 accumulators; the four lanes of a key are merged at the end in
-// fp64.
+// Step 2 (bf16, MFMA): column sums over the text rows of the group for
+// kColsPerScoreWg visual keys.  S = Q K^T with rows on the M side and keys
+// on the N side: each wave keeps kColKB blocks of 16 keys as MFMA operands
+// in registers, and the workgroup streams the group's text-query rows and
+// their normalisers through LDS in 64-row tiles by direct-to-LDS copies
+// (kColBufs buffers, kColBufs - 1 tiles in flight, so the copies hide the
+// L2 latency).  Each lane owns one key per block and sums its rows: fp32
+// within a tile, fp64 across tiles, the four lanes of a key merged at the
+// end in fp64.  Few registers per wave let four waves share each SIMD, so
+// one wave's exponentials run while another's MFMAs do.
+//
+// The normalisers come from col_prep: per head group, scaled to base 2 and
+// padded with +inf (probability 0) to whole tiles.
+//
+// The rows of a head group may be cut into n_split contiguous ranges of
+// tiles (work item = KV head, row range, key block) so that the grid fills
+// whole rounds of the machine; each range then writes fp64 partial sums and
+// col_finalize adds the ranges in order.
+constexpr int kColMaxSplit = 4;      // row ranges per head group, at most
+constexpr int kColSlots = 256 * kColOcc;   // step-2 workgroups resident at once (256 CUs)
+
+// lsep[g][rho] = factor * lse[g * R + rho] for rho < R, +inf up to R_pad.
+__global__ void col_prep(const float* __restrict__ lse, float factor, int R, int R_pad, int n,
+                         float* __restrict__ lsep) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int g = i / R_pad, rho = i % R_pad;
+  lsep[i] = rho < R ? lse[(size_t)g * R + rho] * factor : INFINITY;
+}
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restrict__ qt,
-                                                        const uint16_t* __restrict__ k, Geo geo,
-                                                        const float* __restrict__ lse,
-                                                        float lse_factor, int n_ct,
-                                                        float* __restrict__ scores) {
-  constexpr int KST = D / 32, CPR = D / 8, KPT = 64 * CPR / 256;
-  constexpr int KB = kColKB;
-  __shared__ __align__(16) uint16_t Qs0[64 * D];
-  __shared__ __align__(16) uint16_t Qs1[64 * D];
-  __shared__ float Ls[2][64];
-  const int n_items = geo.hkv * n_ct;
+__global__ __launch_bounds__(kColThreads, kColOcc) void colscore_mfma(
+    const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, Geo geo,
+    const float* __restrict__ lsep, int n_ct, int n_split, float* __restrict__ scores,
+    double* __restrict__ part) {
+  constexpr int KST = D / 32, CPR = D / 8, LPT = 64 * CPR / kColThreads;
+  static_assert(LPT * kColThreads == 64 * CPR, "a tile is a whole number of copies per thread");
+  constexpr int KB = kColKB, NB = kColBufs;
+  constexpr int TILE = 64 * D;
+  constexpr int OPS = LPT + 1;         // copies per thread and tile (rows + normalisers)
+  __shared__ __align__(16) uint16_t Qs[NB * TILE];
+  __shared__ __align__(16) float Ls[NB * 64];
+  const int n_items = geo.hkv * n_split * n_ct;
   const int item = xcd_item(blockIdx.x, n_items);
   if (item >= n_items) return;
-  const int ct = item % n_ct, g = item / n_ct;
+  const int ct = item % n_ct, sp = (item / n_ct) % n_split, g = item / (n_ct * n_split);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int R = geo.G * geo.n_text;
+  const int n_rt = (R + 63) / 64;
+  const int R_pad = n_rt * 64;
+  const int rt0 = (int)((long)sp * n_rt / n_split), rt1 = (int)((long)(sp + 1) * n_rt / n_split);
 
   // key operands: B[k = d][n = key], key = base + kb*16 + col (clamped)
   bf16x8_t kbop[KB][KST];
@@ -489,20 +516,31 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
   for (int kb = 0; kb < KB; ++kb) acc[kb] = 0.0;
 
   const uint16_t* qg = qt + (size_t)g * R * D;
-  const float* lg = lse + (size_t)g * R;
-  int rrow[KPT], rslot[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int cl = tid + 256 * u;
-    rrow[u] = cl / CPR;
-    rslot[u] = cl % CPR;
-  }
-  // row normalisers: rows past the end get +inf (probability 0)
-  auto lse_of = [&](int row) { return row < R ? lg[row] * lse_factor : INFINITY; };
+  const float* lg = lsep + (size_t)g * R_pad;
+  const float c = geo.c;
+  const int r0 = rt0 * 64;
 
-  // one 64-row tile: four 16-row blocks; a block's 16 MFMAs are issued
-  // before the previous block's exponentials are summed
-  auto tile = [&](const uint16_t* Qs, const float* L) {
+  // Direct-to-LDS copies of tile tt of the range into buffer tt % NB:
+  // rows clamped to R - 1, K-swizzled (thread tid fills 16-byte slots
+  // kColThreads*u + tid; a slot's row and physical chunk give the logical
+  // chunk through the self-inverse XOR swizzle), and the tile's 64
+  // normalisers (every wave copies them, so all threads count the same
+  // number of copies; tiles past the range re-read the last one).
+  auto issue = [&](int tt) {
+    const int buf = tt & (NB - 1);
+    const int row0 = r0 + tt * 64;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int slot = kColThreads * u + tid;
+      const int row = slot / CPR, phys = slot % CPR;
+      const uint16_t* src =
+          qg + (size_t)min(row0 + row, R - 1) * D + (Tile<D>::slot_k(row, phys) << 3);
+      dma16(src, lds_addr(Qs + buf * TILE) + (kColThreads * u + 64 * wave) * 16);
+    }
+    dma4(lg + min(row0, R_pad - 64) + lane, lds_addr(Ls + buf * 64));
+  };
+
+  auto tile = [&](const uint16_t* Qt, const float* L) {
     float cs[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) cs[kb] = 0.f;
@@ -511,10 +549,8 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
       u32x4_t a[KST];
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk)
-        a[kk] = *reinterpret_cast<const u32x4_t*>(Qs + Tile<D>::off_k(qb * 16 + col, KST * grp + kk));
-      float lrow[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lrow[i] = L[qb * 16 + 4 * grp + i];
+        a[kk] = *reinterpret_cast<const u32x4_t*>(Qt + Tile<D>::off_k(qb * 16 + col, KST * grp + kk));
+      const floatx4_t lrow = *reinterpret_cast<const floatx4_t*>(L + qb * 16 + 4 * grp);
       floatx4_t sv[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -526,33 +562,37 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs[kb] += fast_exp2(fmaf(sv[kb][i], geo.c, -lrow[i]));
+        for (int i = 0; i < 4; ++i) cs[kb] += fast_exp2(fmaf(sv[kb][i], c, -lrow[i]));
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) acc[kb] += (double)cs[kb];
   };
 
-  const int ntiles = (R + 63) / 64;
-  u32x4_t ra[KPT], rb_[KPT];
-  float la = 0.f, lb = 0.f;
-  tile_load<D, KPT>(ra, qg, 0, R - 1, rrow, rslot);
-  tile_store<D, KPT>(ra, Qs0, rrow, rslot);
-  if (tid < 64) Ls[0][tid] = lse_of(tid);
-  tile_load<D, KPT>(ra, qg, 64, R - 1, rrow, rslot);
-  tile_load<D, KPT>(rb_, qg, 128, R - 1, rrow, rslot);
-  if (tid < 64) { la = lse_of(64 + tid); lb = lse_of(128 + tid); }
-  for (int t = 0; t < ntiles; t += 2) {
+  // Step t waits for its own copies of tile t (the NB - 2 newer tiles may
+  // stay in flight), then after the barrier -- all copies of tile t have
+  // landed and every wave is done with the buffer of tile t - 1 -- refills
+  // that buffer with tile t + NB - 1.  A copy is issued at every step, so
+  // the count in flight is the same at every wait.
+  const int ntiles = rt1 - rt0;
+  // the key operands land before any copy is issued (the empty asm takes
+  // them as operands, so their loads complete here and stay here): the
+  // compiler does not count the copies, so a wait it placed for these loads
+  // inside the loop would also wait for every copy in flight
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) asm volatile("" : "+v"(kbop[kb][kk]));
+#pragma unroll
+  for (int tt = 0; tt < NB - 1; ++tt) issue(tt);
+  for (int t = 0; t < ntiles; ++t) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 2) * OPS));
     __syncthreads();
-    tile_store<D, KPT>(ra, Qs1, rrow, rslot);
-    if (tid < 64) { Ls[1][tid] = la; la = lse_of((t + 3) * 64 + tid); }
-    tile_load<D, KPT>(ra, qg, (t + 3) * 64, R - 1, rrow, rslot);
-    tile(Qs0, Ls[0]);
-    __syncthreads();
-    tile_store<D, KPT>(rb_, Qs0, rrow, rslot);
-    if (tid < 64) { Ls[0][tid] = lb; lb = lse_of((t + 4) * 64 + tid); }
-    tile_load<D, KPT>(rb_, qg, (t + 4) * 64, R - 1, rrow, rslot);
-    if (t + 1 < ntiles) tile(Qs1, Ls[1]);
+    issue(t + NB - 1);
+    const int buf = t & (NB - 1);
+    tile(Qs + buf * TILE, Ls + buf * 64);
   }
+  // no copy may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   const double inv = 1.0 / ((double)geo.G * (double)geo.n_text);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -560,8 +600,39 @@ __global__ __launch_bounds__(256, 2) void colscore_mfma(const uint16_t* __restri
     a += __shfl_xor(a, 16, kWave);
     a += __shfl_xor(a, 32, kWave);
     const int j = ct * kColsPerScoreWg + wave * 16 * KB + kb * 16 + col;
-    if (grp == 0 && j < geo.vis_len) scores[(size_t)g * geo.vis_len + j] = (float)(a * inv);
+    if (grp == 0 && j < geo.vis_len) {
+      if (n_split == 1)
+        scores[(size_t)g * geo.vis_len + j] = (float)(a * inv);
+      else
+        part[((size_t)sp * geo.hkv + g) * geo.vis_len + j] = a;
+    }
   }
+}
+
+// Adds the n_split fp64 partial column sums of each key in range order.
+__global__ void col_finalize(const double* __restrict__ part, int n_split, int n, double inv,
+                             float* __restrict__ scores) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  double a = 0.0;
+  for (int s = 0; s < n_split; ++s) a += part[(size_t)s * n + j];
+  scores[j] = (float)(a * inv);
+}
+
+// Row ranges for step 2: the count with the least time, in units of one
+// tile per workgroup, when the grid runs in rounds of kColSlots workgroups.
+int col_splits(int n_items, int n_rt) {
+  int best = 1;
+  long best_cost = -1;
+  for (int s = 1; s <= kColMaxSplit && s <= n_rt; ++s) {
+    const long rounds = ((long)n_items * s + kColSlots - 1) / kColSlots;
+    const long cost = rounds * ((n_rt + s - 1) / s);
+    if (best_cost < 0 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // Step 2 (vector ALU): one wave per 64 visual keys; lane j keeps key j in
@@ -761,7 +832,7 @@ __global__ __launch_bounds__(kTopkThreads) void radix_topk(const float* __restri
 
 template <int D>
 hipError_t launch_mfma_select(const SelectArgs& a, const Geo& geo, float* lse2, float* m_part,
-                              double* l_part, hipStream_t st) {
+                              double* l_part, double* col_part, float* lsep, hipStream_t st) {
   const auto* qt = static_cast<const uint16_t*>(a.q_text);
   const auto* k = static_cast<const uint16_t*>(a.k);
   const float* lse = lse2;
@@ -781,9 +852,21 @@ hipError_t launch_mfma_select(const SelectArgs& a, const Geo& geo, float* lse2, 
     lse_finalize<<<(rows + 255) / 256, 256, 0, st>>>(m_part, l_part, n_chunks, rows, lse2);
   }
   const int n_ct = (a.vis_len + kColsPerScoreWg - 1) / kColsPerScoreWg;
-  const int n_items = a.hkv * n_ct;
+  const int R = geo.G * a.n_text;
+  const int n_rt = (R + 63) / 64;
+  const int n_split = col_splits(a.hkv * n_ct, n_rt);
+  const int n_items = a.hkv * n_ct * n_split;
   const int grid = ((n_items + kXcds - 1) / kXcds) * kXcds;
-  colscore_mfma<D><<<grid, 256, 0, st>>>(qt, k, geo, lse, factor, n_ct, a.scores_out);
+  const int n_lsep = a.hkv * n_rt * 64;
+  col_prep<<<(n_lsep + 255) / 256, 256, 0, st>>>(lse, factor, R, n_rt * 64, n_lsep, lsep);
+  colscore_mfma<D><<<grid, kColThreads, 0, st>>>(qt, k, geo, lsep, n_ct, n_split, a.scores_out,
+                                                 col_part);
+  if (n_split > 1) {
+    const int n = a.hkv * a.vis_len;
+    col_finalize<<<(n + 255) / 256, 256, 0, st>>>(col_part, n_split, n,
+                                                   1.0 / ((double)geo.G * (double)a.n_text),
+                                                   a.scores_out);
+  }
   return hipGetLastError();
 }
 
@@ -805,7 +888,7 @@ hipError_t launch_valu_select(const SelectArgs& a, const Geo& geo, float* lse2, 
 }
 
 struct SelectLayout {
-  size_t lse2, m_part, l_part, scores, total;
+  size_t lse2, m_part, l_part, col_part, lsep, scores, total;
 };
 
 SelectLayout select_layout(int hq, int hkv, int n_text, int vis_len, int text_start,
@@ -820,6 +903,10 @@ SelectLayout select_layout(int hq, int hkv, int n_text, int vis_len, int text_st
   off += align256((size_t)n_chunks * rows * sizeof(float));
   L.l_part = off;
   off += align256((size_t)n_chunks * rows * sizeof(double));
+  L.col_part = off;
+  off += align256((size_t)kColMaxSplit * hkv * vis_len * sizeof(double));
+  L.lsep = off;
+  off += align256((size_t)hkv * (((size_t)(hq / hkv) * n_text + 63) / 64) * 64 * sizeof(float));
   L.scores = off;
   if (scores_in_ws) off += align256((size_t)hkv * vis_len * sizeof(float));
   L.total = off;
@@ -841,13 +928,15 @@ hipError_t launch_select(const SelectArgs& a0, hipStream_t st) {
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* m_part = reinterpret_cast<float*>(ws + L.m_part);
   double* l_part = reinterpret_cast<double*>(ws + L.l_part);
+  double* col_part = reinterpret_cast<double*>(ws + L.col_part);
+  float* lsep = reinterpret_cast<float*>(ws + L.lsep);
   if (!a.scores_out) a.scores_out = reinterpret_cast<float*>(ws + L.scores);
   Geo geo{a.hq, a.hkv, a.hq / a.hkv, a.d, a.capacity, a.text_start, a.n_text,
           a.vis_start, a.vis_len, a.scale * kLog2e};
   hipError_t err;
   if (a.bf16)
-    err = a.d == 128 ? launch_mfma_select<128>(a, geo, lse2, m_part, l_part, st)
-                     : launch_mfma_select<64>(a, geo, lse2, m_part, l_part, st);
+    err = a.d == 128 ? launch_mfma_select<128>(a, geo, lse2, m_part, l_part, col_part, lsep, st)
+                     : launch_mfma_select<64>(a, geo, lse2, m_part, l_part, col_part, lsep, st);
   else
     err = a.d == 128 ? launch_valu_select<float, 128>(a, geo, lse2, st)
                      : launch_valu_select<float, 64>(a, geo, lse2, st);
