@@ -433,22 +433,25 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
   const int last = kl.pos(n_entries - 1);   // a valid row for the padded entries
+  // gathered rows load in their natural chunk order (short address path
+  // after the index read); the swizzle is applied to the LDS stores
   u32x4_t kreg[NL], vreg[NL];
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     const int cl = lane + 64 * u;
-    const int row = cl / CPR, slot = cl % CPR;
+    const int row = cl / CPR, chunk = cl % CPR;
     int pr = pw[row];
     pr = pr >= 0 ? pr : last;
-    const size_t base = (size_t)pr * D;
-    kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base + (Tile<D>::slot_k(row, slot) << 3));
-    vreg[u] = *reinterpret_cast<const u32x4_t*>(vh + base + (Tile<D>::slot_v(row, slot) << 3));
+    const size_t base = (size_t)pr * D + (chunk << 3);
+    kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base);
+    vreg[u] = *reinterpret_cast<const u32x4_t*>(vh + base);
   }
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     const int cl = lane + 64 * u;
-    *reinterpret_cast<u32x4_t*>(Ks + (cl / CPR) * D + ((cl % CPR) << 3)) = kreg[u];
-    *reinterpret_cast<u32x4_t*>(Vs + (cl / CPR) * D + ((cl % CPR) << 3)) = vreg[u];
+    const int row = cl / CPR, chunk = cl % CPR;
+    *reinterpret_cast<u32x4_t*>(Ks + Tile<D>::off_k(row, chunk)) = kreg[u];
+    *reinterpret_cast<u32x4_t*>(Vs + Tile<D>::off_v(row, chunk)) = vreg[u];
   }
   // the wave reads back only its own region: no workgroup barrier needed
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS stores done

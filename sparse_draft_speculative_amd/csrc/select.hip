@@ -48,27 +48,6 @@ struct Geo {
   float c;  // scale * log2 e
 };
 
-// Stage one 64-row tile of a [rows][D] bf16 tensor: global -> registers
-// (rows clamped to ``last``, so every load is in bounds) and registers ->
-// LDS in the K-swizzled layout of Tile<D>.
-template <int D, int KPT>
-__device__ __forceinline__ void tile_load(u32x4_t (&r)[KPT], const uint16_t* base, int row0,
-                                          int last, const int (&rrow)[KPT],
-                                          const int (&rslot)[KPT]) {
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const size_t off = (size_t)min(row0 + rrow[u], last) * D;
-    r[u] = *reinterpret_cast<const u32x4_t*>(base + off + (Tile<D>::slot_k(rrow[u], rslot[u]) << 3));
-  }
-}
-template <int D, int KPT>
-__device__ __forceinline__ void tile_store(const u32x4_t (&r)[KPT], uint16_t* lds,
-                                           const int (&rrow)[KPT], const int (&rslot)[KPT]) {
-#pragma unroll
-  for (int u = 0; u < KPT; ++u)
-    *reinterpret_cast<u32x4_t*>(lds + rrow[u] * D + (rslot[u] << 3)) = r[u];
-}
-
 // ---------------------------------------------------------------------------
 // Step 1 (bf16, MFMA): partial (max, sum) of each text row over one key chunk.
 //
@@ -103,7 +82,7 @@ __device__ __forceinline__ void lse_issue_tile(uint16_t* buf, const uint16_t* kh
   for (int u = 0; u < LPT; ++u) {
     const int slot = 256 * u + tid;
     const int row = slot / CPR, phys = slot % CPR;
-    const int logical = phys ^ (row % CPR);
+    const int logical = Tile<D>::slot_k(row, phys);
     const uint16_t* src = kh + (size_t)min(t0 + row, last) * D + logical * 8;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + (256 * u + 64 * wave) * 8), 16, 0,
                                      0);

@@ -31,18 +31,26 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 }
 
 // LDS tiles of 64 K or V rows, row-major, with the 16-byte chunks of each
-// row permuted (XOR swizzle) so that the reads feeding one MFMA operand hit
-// distinct banks:
-//  * K: chunk c of row r sits at slot c ^ (r % CPR).  A K-operand read takes
-//    one chunk of 16 consecutive rows.
-//  * V: chunk c of row r sits at slot c ^ 2*(r % 4).  A transpose read takes
-//    8 bytes from 4 consecutive rows x 2 chunks per 16 lanes; the XOR with
-//    2*(r % 4) spreads those over 8 distinct slots.
+// row permuted (XOR swizzle, self-inverse) so that the reads feeding one
+// MFMA operand hit distinct banks (measured on the device with the LDS
+// bank-conflict counter):
+//  * K: chunk c of row r sits at slot c ^ kx(r), kx(r) = (r % 4) * CPR/4 +
+//    (r / 4) % (CPR/4).  A K-operand read takes one chunk of 16
+//    consecutive rows per 16 lanes.
+//  * V: chunk c of row r sits at slot c ^ vx(r), vx(r) = 2 (r % 8) for
+//    D = 128 and 2 (r % 4) for D = 64.  A transpose read takes 8 bytes from
+//    4 consecutive rows x 2 chunks per 16 lanes.
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static __device__ __forceinline__ int slot_k(int row, int chunk) { return chunk ^ (row % CPR); }
-  static __device__ __forceinline__ int slot_v(int row, int chunk) { return chunk ^ ((row & 3) << 1); }
+  static __device__ __forceinline__ int kx(int row) {
+    return (row & 3) * (CPR / 4) + ((row >> 2) & (CPR / 4 - 1));
+  }
+  static __device__ __forceinline__ int vx(int row) {
+    return D == 128 ? (row & 7) << 1 : (row & 3) << 1;
+  }
+  static __device__ __forceinline__ int slot_k(int row, int chunk) { return chunk ^ kx(row); }
+  static __device__ __forceinline__ int slot_v(int row, int chunk) { return chunk ^ vx(row); }
   static __device__ __forceinline__ int off_k(int row, int chunk) {   // elements
     return row * D + (slot_k(row, chunk) << 3);
   }
