@@ -51,222 +51,140 @@ struct Geo {
 // ---------------------------------------------------------------------------
 // Step 1 (bf16, MFMA): partial (max, sum) of each text row over one key chunk.
 //
-// Work item = (KV head, key chunk, 128-row block).  Keys move global -> LDS
-// in 64-key tiles by direct-to-LDS loads (three buffers, two tiles in
-// flight).  Wave w takes key half w & 1 (32 keys) of every tile against row
-// half w >> 1 (64 rows), whose Q operands stay in registers, so every key
-// fragment read from LDS feeds four MFMA column blocks.  Scores are
-// S^T = K Q^T (keys on the M side).  Each lane keeps a running (max, sum)
-// per row over the keys it sees; the max moves only when a score exceeds it
-// by 2^8 (exact: it only shifts the exponent).  Sums run in fp32 within
-// three tiles and in fp64 across them.  Lane groups and the two key halves
-// are merged once at the end.  Only tiles that reach the causal (text) part
-// or the chunk end are masked.
-constexpr int kLseNB = 4;                      // 16-row column blocks per wave
-constexpr int kLseRows = 32 * kLseNB;          // text rows per workgroup (two row halves)
-constexpr int kLseKB = 2;                      // 16-key blocks per wave and tile
-static_assert(kLseKB == 2, "the tile sum below adds 4 * kLseKB = 8 terms");
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Issue the direct-to-LDS loads of one 64-key tile.  Thread tid's u-th
-// 16-byte slot is s = 256u + tid (each wave instruction fills 64
-// consecutive slots); the slot's row and physical chunk give the logical
-// chunk through the K swizzle, and rows past the end re-read the last key.
-template <int D>
-__device__ __forceinline__ void lse_issue_tile(uint16_t* buf, const uint16_t* kh, int t0,
-                                               int last, int tid, int wave) {
-  constexpr int CPR = D / 8;
-  constexpr int LPT = 64 * CPR / 256;
-#pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int slot = 256 * u + tid;
-    const int row = slot / CPR, phys = slot % CPR;
-    const int logical = Tile<D>::slot_k(row, phys);
-    const uint16_t* src = kh + (size_t)min(t0 + row, last) * D + logical * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + (256 * u + 64 * wave) * 8), 16, 0,
-                                     0);
-  }
-}
+// Work item = (KV head, key chunk, kLseRowsWg-row block).  Each wave keeps
+// kLseRB blocks of 16 text rows as MFMA operands in registers; the
+// workgroup streams the chunk's keys through LDS in 64-key tiles by
+// direct-to-LDS copies (kLseBufs buffers, kLseBufs - 1 tiles in flight).
+// Scores are S^T = K Q^T (keys on the M side), so each key fragment read
+// from LDS feeds kLseRB MFMA column blocks and lane (col, grp) gets keys
+// 4 grp + i of every 16-key block for row col.  Each lane keeps a running
+// (max, sum) per row block over the keys it sees; the max moves only when
+// a score exceeds it by 2^8 (exact: it only shifts the exponent).  The sum
+// of a tile is fp32, the running sum fp64.  The four lanes of a row are
+// merged once at the end.  Only tiles that reach the causal (text) part or
+// the chunk end are masked.
+constexpr int kLseRB = 2;                          // 16-row blocks per wave
+constexpr int kLseWaves = 8;                       // waves per workgroup
+constexpr int kLseThreads = 64 * kLseWaves;
+constexpr int kLseOcc = 2;                         // workgroups per CU (the launch bound
+                                                   // asks for the matching waves per SIMD)
+constexpr int kLseBufs = 4;                        // LDS key-tile buffers (a power of two)
+constexpr int kLseRowsWg = kLseWaves * 16 * kLseRB;   // text rows per workgroup
 
 struct LseState {
-  float m[kLseNB];      // running max (base-2 units) per row block
-  float l32[kLseNB];    // sum relative to m since the last flush
-  double l[kLseNB];     // flushed sum relative to m
+  float m[kLseRB];      // running max (base-2 units) per row block
+  double l[kLseRB];     // sum relative to m
 };
-
-// Slow path for one row block, taken by the whole wave (MFMA operands and
-// results cover every lane, so no MFMA may sit under a lane-dependent
-// branch): lanes with need set take the max of their scores, move m when it
-// exceeds m + 8 and recompute the tile sum; other lanes keep ``fast``.
-// Written with selects only.
-template <int N>
-__device__ __forceinline__ float lse_rescue(const float (&v)[N], float c, LseState& st, int nb,
-                                            float fast) {
-  const bool need = !(fast <= 256.f);
-  float tmax = v[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) tmax = fmaxf(tmax, v[i]);
-  const float ts = tmax * c;                     // c > 0: max then scale
-  const bool move = need && tmax != -INFINITY && ts > st.m[nb] + 8.f;
-  const bool had = st.m[nb] != -INFINITY;
-  const double scale = exp2((double)(had ? st.m[nb] : ts) - (double)ts);
-  const double lnew = (st.l[nb] + (double)st.l32[nb]) * scale;
-  st.l[nb] = move ? lnew : st.l[nb];
-  st.l32[nb] = move ? 0.f : st.l32[nb];
-  st.m[nb] = move ? ts : st.m[nb];
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < N; ++i) t += fast_exp2(fmaf(v[i], c, -st.m[nb]));
-  t = tmax == -INFINITY ? 0.f : t;
-  return need ? t : fast;
-}
 
 // Where a tile reaches the chunk end or the causal part, the scores of keys
-// past key1 or after the row's own position are -inf.  Row rho of the
-// block is text row rho % n_text (the G heads' rows are stacked).
+// at or past key1 or after the row's own position are -inf.  Row rho of the
+// group is text row rho % n_text (the G heads' rows are stacked).
 struct LseMask {
   int key1, R, n_text, text_start;
-  __device__ __forceinline__ void apply(float (&v)[4 * kLseKB], int rho, int key_base) const {
+  __device__ __forceinline__ void apply(floatx4_t& v, int rho, int key_base) const {
     const int rpos = text_start + (rho < R ? rho % n_text : 0);
 #pragma unroll
-    for (int j = 0; j < 4 * kLseKB; ++j) {
-      const int key = key_base + (j >> 2) * 16 + (j & 3);
-      if (!(key < key1 && key <= rpos)) v[j] = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const int key = key_base + i;
+      if (!(key < key1 && key <= rpos)) v[i] = -INFINITY;
     }
   }
 };
 
-// The wave's key fragments of one tile (kLseKB x KST 16-byte reads at the
-// byte addresses ``addr`` plus the buffer offset OFF).  The reads sit in one
-// asm block that also waits for them: the compiler, which cannot tell the
-// three buffers apart, would otherwise wait for every direct-to-LDS load in
-// flight (including the ones filling other buffers) before any LDS read.
-template <int OFF>
-__device__ __forceinline__ void lse_frag_read(u32x4_t (&a)[8], const uint32_t (&addr)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:%16\n\t"
-      "ds_read_b128 %1, %9 offset:%16\n\t"
-      "ds_read_b128 %2, %10 offset:%16\n\t"
-      "ds_read_b128 %3, %11 offset:%16\n\t"
-      "ds_read_b128 %4, %12 offset:%16\n\t"
-      "ds_read_b128 %5, %13 offset:%16\n\t"
-      "ds_read_b128 %6, %14 offset:%16\n\t"
-      "ds_read_b128 %7, %15 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
-        "=&v"(a[6]), "=&v"(a[7])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]),
-        "v"(addr[6]), "v"(addr[7]), "i"(OFF));
-}
-template <int OFF>
-__device__ __forceinline__ void lse_frag_read(u32x4_t (&a)[4], const uint32_t (&addr)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%8\n\t"
-      "ds_read_b128 %1, %5 offset:%8\n\t"
-      "ds_read_b128 %2, %6 offset:%8\n\t"
-      "ds_read_b128 %3, %7 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF));
+// The scores of one 16-key block (LDS rows kb*16 ..) against the wave's row
+// blocks: v[rb] holds keys 4 grp + i for row col of block rb.
+template <int D, bool MASK>
+__device__ __forceinline__ void lse_block(const uint16_t* Kt, const bf16x8_t (*qb)[D / 32], int kb,
+                                          int col, int grp, const LseMask& mk, int row0,
+                                          int key_base, floatx4_t (&v)[kLseRB]) {
+  constexpr int KST = D / 32;
+  u32x4_t a[KST];
+#pragma unroll
+  for (int kk = 0; kk < KST; ++kk)
+    a[kk] = *reinterpret_cast<const u32x4_t*>(Kt + Tile<D>::off_k(kb * 16 + col, KST * grp + kk));
+#pragma unroll
+  for (int rb = 0; rb < kLseRB; ++rb) {
+    floatx4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) x = mfma_bf16(as_bf16x8(a[kk]), qb[rb][kk], x);
+    if constexpr (MASK) mk.apply(x, row0 + rb * 16 + col, key_base);
+    v[rb] = x;
+  }
 }
 
-// One wave's share of one tile: key blocks 2*kh, 2*kh+1 of the tile in LDS
-// buffer OFF against the wave's kLseNB row blocks.  The scores of a row
-// block live only until their exps are taken; the rare slow path recomputes
-// them.
-template <int D, int OFF, bool MASK>
-__device__ __forceinline__ void lse_step(const uint32_t (&addr)[kLseKB * D / 32],
-                                         const bf16x8_t (*qb)[D / 32], int t0, const LseMask& mk,
-                                         int row0, float c, int grp, int col, int kh,
+// One 64-key tile.  Fast path: the probabilities relative to the running
+// max are summed directly; each is at most 2^8 while the max invariant
+// holds, so a tile sum above 2^8 (or NaN: an unset max against a masked
+// score) flags a lane whose max may have to move.  Then the whole wave (the
+// MFMAs cover every lane, so none may sit under a lane-dependent branch)
+// takes the slow path: it recomputes the tile's scores block by block and,
+// for the flagged lanes, moves the max to a block's max where that exceeds
+// max + 8 (rescaling the running and the partial tile sum) before adding
+// the block; all with selects.
+template <int D, bool MASK>
+__device__ __forceinline__ void lse_tile(const uint16_t* Kt, const bf16x8_t (*qb)[D / 32], int t0,
+                                         const LseMask& mk, int row0, float c, int col, int grp,
                                          LseState& st) {
-  constexpr int KST = D / 32;
-  u32x4_t af[kLseKB * KST];
-  lse_frag_read<OFF>(af, addr);
-  u32x4_t a[kLseKB][KST];
+  float tot[kLseRB];
 #pragma unroll
-  for (int kb = 0; kb < kLseKB; ++kb)
+  for (int rb = 0; rb < kLseRB; ++rb) tot[rb] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) a[kb][kk] = af[kb * KST + kk];
-  const int key_base = t0 + kLseKB * kh * 16 + 4 * grp;
-  float tot[kLseNB];
+  for (int kb = 0; kb < 4; ++kb) {
+    floatx4_t v[kLseRB];
+    lse_block<D, MASK>(Kt, qb, kb, col, grp, mk, row0, t0 + kb * 16 + 4 * grp, v);
 #pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) {
-    float v[4 * kLseKB];
+    for (int rb = 0; rb < kLseRB; ++rb)
 #pragma unroll
-    for (int kb = 0; kb < kLseKB; ++kb) {
-      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kb][kk]), qb[nb][kk], acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[4 * kb + i] = acc[i];
-    }
-    if constexpr (MASK) mk.apply(v, row0 + nb * 16 + col, key_base);
-    float p[4 * kLseKB];
-#pragma unroll
-    for (int j = 0; j < 4 * kLseKB; ++j) p[j] = fast_exp2(fmaf(v[j], c, -st.m[nb]));
-    // pairwise sum of the 8 terms
-    tot[nb] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      for (int i = 0; i < 4; ++i) tot[rb] += fast_exp2(fmaf(v[rb][i], c, -st.m[rb]));
   }
-  // every term <= 2^8 keeps the running-max invariant; NaN (an unset max
-  // against a masked score) and overflow fail the test and take the slow path
   bool ok = true;
 #pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) ok = ok && (tot[nb] <= 256.f);
-  if (__any(!ok)) {                    // wave-uniform: the MFMAs below run on every lane
+  for (int rb = 0; rb < kLseRB; ++rb) ok = ok && (tot[rb] <= 256.f);
+  if (__any(!ok)) {                    // wave-uniform
+    bool need[kLseRB];
+    float t2[kLseRB];
 #pragma unroll
-    for (int nb = 0; nb < kLseNB; ++nb) {
-      float v[4 * kLseKB];
-#pragma unroll
-      for (int kb = 0; kb < kLseKB; ++kb) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kb][kk]), qb[nb][kk], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 * kb + i] = acc[i];
-      }
-      if constexpr (MASK) mk.apply(v, row0 + nb * 16 + col, key_base);
-      tot[nb] = lse_rescue(v, c, st, nb, tot[nb]);
+    for (int rb = 0; rb < kLseRB; ++rb) {
+      need[rb] = !(tot[rb] <= 256.f);
+      t2[rb] = 0.f;
     }
+#pragma unroll 1
+    for (int kb = 0; kb < 4; ++kb) {
+      floatx4_t v[kLseRB];
+      lse_block<D, MASK>(Kt, qb, kb, col, grp, mk, row0, t0 + kb * 16 + 4 * grp, v);
+#pragma unroll
+      for (int rb = 0; rb < kLseRB; ++rb) {
+        const float bm = fmaxf(fmaxf(v[rb][0], v[rb][1]), fmaxf(v[rb][2], v[rb][3]));
+        const float ts = bm * c;       // c > 0: max then scale
+        const bool move = need[rb] && bm != -INFINITY && ts > st.m[rb] + 8.f;
+        const bool had = st.m[rb] != -INFINITY;
+        const double scale = exp2((double)(had ? st.m[rb] : ts) - (double)ts);
+        st.l[rb] = move ? st.l[rb] * scale : st.l[rb];
+        t2[rb] = move ? (float)((double)t2[rb] * scale) : t2[rb];
+        st.m[rb] = move ? ts : st.m[rb];
+        float b = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b += fast_exp2(fmaf(v[rb][i], c, -st.m[rb]));
+        t2[rb] += bm == -INFINITY ? 0.f : b;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < kLseRB; ++rb) tot[rb] = need[rb] ? t2[rb] : tot[rb];
   }
 #pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) st.l32[nb] += tot[nb];
+  for (int rb = 0; rb < kLseRB; ++rb) st.l[rb] += (double)tot[rb];
 }
-
-__device__ __forceinline__ void lse_flush(LseState& st) {
-#pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) {
-    st.l[nb] += (double)st.l32[nb];
-    st.l32[nb] = 0.f;
-  }
-}
-
-template <int D, int OFF>
-__device__ __forceinline__ void lse_tile(const uint32_t (&addr)[kLseKB * D / 32],
-                                         const bf16x8_t (*qb)[D / 32], int t0, const LseMask& mk,
-                                         int row0, float c, int grp, int col, int kh,
-                                         LseState& st) {
-  if (t0 + 64 <= mk.text_start && t0 + 64 <= mk.key1)
-    lse_step<D, OFF, false>(addr, qb, t0, mk, row0, c, grp, col, kh, st);
-  else
-    lse_step<D, OFF, true>(addr, qb, t0, mk, row0, c, grp, col, kh, st);
-}
-
-constexpr int kLseOcc = 2;                     // workgroups per CU
 
 template <int D>
-__global__ __launch_bounds__(256, kLseOcc) void lse_partial_mfma(const uint16_t* __restrict__ qt,
-                                                           const uint16_t* __restrict__ k, Geo geo,
-                                                           int n_chunks, int n_rb,
-                                                           float* __restrict__ m_part,
-                                                           double* __restrict__ l_part) {
-  constexpr int KST = D / 32;
-  constexpr int LPT = 64 * (D / 8) / 256;      // direct-to-LDS loads per thread per tile
-  constexpr int TB = 64 * D * 2;                // bytes of one tile buffer
-  __shared__ __align__(16) uint16_t Kbuf[3 * 64 * D];
-  uint16_t* Kb0 = Kbuf;
-  uint16_t* Kb1 = Kbuf + 64 * D;
-  uint16_t* Kb2 = Kbuf + 2 * 64 * D;
+__global__ __launch_bounds__(kLseThreads, kLseOcc * kLseWaves / 4) void lse_partial_mfma(
+    const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, Geo geo, int n_chunks,
+    int n_rb, float* __restrict__ m_part, double* __restrict__ l_part) {
+  constexpr int KST = D / 32, CPR = D / 8;
+  constexpr int LPT = 64 * CPR / kLseThreads;   // direct-to-LDS copies per thread and tile
+  static_assert(LPT * kLseThreads == 64 * CPR, "a tile is a whole number of copies per thread");
+  constexpr int NB = kLseBufs;
+  constexpr int TILE = 64 * D;
+  __shared__ __align__(16) uint16_t Kbuf[NB * TILE];
   const int n_items = geo.hkv * n_chunks * n_rb;
   const int item = xcd_item(blockIdx.x, n_items);
   if (item >= n_items) return;
@@ -276,31 +194,30 @@ __global__ __launch_bounds__(256, kLseOcc) void lse_partial_mfma(const uint16_t*
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int kh = wave & 1, rh = wave >> 1;     // key half, row half
   const int R = geo.G * geo.n_text;
   const int n_keys = geo.text_start + geo.n_text;
   const int key0 = ch * kLseChunk, key1 = min(n_keys, key0 + kLseChunk);
-  const int row0 = rb * kLseRows + rh * (kLseRows / 2);   // first row of the wave
+  const int row0 = rb * kLseRowsWg + wave * 16 * kLseRB;   // first row of the wave
 
-  bf16x8_t qb[kLseNB][KST];
+  // Q operands: B[k = d][n = row] (rows past R read as zero; never stored)
+  bf16x8_t qb[kLseRB][KST];
 #pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) {
-    const int rho = row0 + nb * 16 + col;
+  for (int r = 0; r < kLseRB; ++r) {
+    const int rho = row0 + r * 16 + col;
     const bool ok = rho < R;
     const uint16_t* qrow = qt + ((size_t)g * R + (ok ? rho : 0)) * D + (D / 4) * grp;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = *reinterpret_cast<const uint4*>(qrow + 8 * kk);
-      qb[nb][kk] = as_bf16x8(u);
+      u32x4_t u = {0u, 0u, 0u, 0u};
+      if (ok) u = *reinterpret_cast<const u32x4_t*>(qrow + 8 * kk);
+      qb[r][kk] = as_bf16x8(u);
     }
   }
   LseState st;
 #pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) {
-    st.m[nb] = -INFINITY;
-    st.l32[nb] = 0.f;
-    st.l[nb] = 0.0;
+  for (int r = 0; r < kLseRB; ++r) {
+    st.m[r] = -INFINITY;
+    st.l[r] = 0.0;
   }
 
   const uint16_t* khp = k + (size_t)g * geo.capacity * D;
@@ -308,72 +225,64 @@ __global__ __launch_bounds__(256, kLseOcc) void lse_partial_mfma(const uint16_t*
   const int last = key1 - 1;
   const LseMask mk{key1, R, geo.n_text, geo.text_start};
   const float c = geo.c;
-  // LDS byte addresses of the wave's key fragments in buffer 0
-  uint32_t addr[kLseKB * KST];
-#pragma unroll
-  for (int kb = 0; kb < kLseKB; ++kb)
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk)
-      addr[kb * KST + kk] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-          Kbuf + Tile<D>::off_k((kLseKB * kh + kb) * 16 + col, KST * grp + kk)));
-  // Three LDS buffers, unrolled by three so every buffer is static.  Step t
-  // waits for its own tile (one newer tile may stay in flight), then after
-  // the barrier refills the buffer read in step t-1 with tile t+2.  Loads
-  // past the last tile re-read valid rows, so the count of loads in flight
-  // is the same at every step.
-  lse_issue_tile<D>(Kb0, khp, key0, last, tid, wave);
-  lse_issue_tile<D>(Kb1, khp, key0 + 64, last, tid, wave);
-  for (int t = 0; t < ntiles; t += 3) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-    __syncthreads();
-    lse_issue_tile<D>(Kb2, khp, key0 + (t + 2) * 64, last, tid, wave);
-    lse_tile<D, 0>(addr, qb, key0 + t * 64, mk, row0, c, grp, col, kh, st);
-    if (t + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-      __syncthreads();
-      lse_issue_tile<D>(Kb0, khp, key0 + (t + 3) * 64, last, tid, wave);
-      lse_tile<D, TB>(addr, qb, key0 + (t + 1) * 64, mk, row0, c, grp, col, kh, st);
-    }
-    if (t + 2 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-      __syncthreads();
-      lse_issue_tile<D>(Kb1, khp, key0 + (t + 4) * 64, last, tid, wave);
-      lse_tile<D, 2 * TB>(addr, qb, key0 + (t + 2) * 64, mk, row0, c, grp, col, kh, st);
-    }
-    lse_flush(st);
-  }
-  // no direct-to-LDS load may still be writing when the buffers are reused
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
 
-  // merge the four lane groups of each row, then the two key halves via LDS
-  constexpr int HALF = kLseRows / 2;
-  float* xm = reinterpret_cast<float*>(Kb0);                      // [4 waves][HALF rows]
-  double* xl = reinterpret_cast<double*>(Kb1);                    // [4 waves][HALF rows]
+  // Direct-to-LDS copies of tile tt of the chunk into buffer tt % NB, rows
+  // clamped to the chunk's last key, K-swizzled (thread tid fills 16-byte
+  // slots kLseThreads*u + tid; a slot's row and physical chunk give the
+  // logical chunk through the self-inverse XOR swizzle).
+  auto issue = [&](int tt) {
+    uint16_t* buf = Kbuf + (tt & (NB - 1)) * TILE;
 #pragma unroll
-  for (int nb = 0; nb < kLseNB; ++nb) {
-    const float mm = max_over_groups(st.m[nb]);
-    double ll = (st.m[nb] == -INFINITY) ? 0.0 : st.l[nb] * exp2((double)st.m[nb] - (double)mm);
+    for (int u = 0; u < LPT; ++u) {
+      const int slot = kLseThreads * u + tid;
+      const int row = slot / CPR, phys = slot % CPR;
+      const uint16_t* src =
+          khp + (size_t)min(key0 + tt * 64 + row, last) * D + (Tile<D>::slot_k(row, phys) << 3);
+      dma16(src, lds_addr(buf) + (kLseThreads * u + 64 * wave) * 16);
+    }
+  };
+
+  // the Q operands land before any copy is issued (the empty asm takes them
+  // as operands): the compiler does not count the copies, so a wait it
+  // placed for these loads inside the loop would also wait for every copy
+  // in flight
+#pragma unroll
+  for (int r = 0; r < kLseRB; ++r)
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) asm volatile("" : "+v"(qb[r][kk]));
+  // Step t waits for its own copies of tile t (the NB - 2 newer tiles may
+  // stay in flight); after the barrier every copy of tile t has landed and
+  // every wave is done with the buffer of tile t - 1, which is refilled with
+  // tile t + NB - 1.  A copy is issued at every step (tiles past the chunk
+  // re-read its last key), so the count in flight is the same at every wait.
+#pragma unroll
+  for (int tt = 0; tt < NB - 1; ++tt) issue(tt);
+  for (int t = 0; t < ntiles; ++t) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 2) * LPT));
+    __syncthreads();
+    issue(t + NB - 1);
+    const uint16_t* Kt = Kbuf + (t & (NB - 1)) * TILE;
+    const int t0 = key0 + t * 64;
+    if (t0 + 64 <= mk.text_start && t0 + 64 <= mk.key1)
+      lse_tile<D, false>(Kt, qb, t0, mk, row0, c, col, grp, st);
+    else
+      lse_tile<D, true>(Kt, qb, t0, mk, row0, c, col, grp, st);
+  }
+  // no copy may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // merge the four lane groups of each row (they saw different keys)
+#pragma unroll
+  for (int r = 0; r < kLseRB; ++r) {
+    const float mm = max_over_groups(st.m[r]);
+    double ll = (st.m[r] == -INFINITY) ? 0.0 : st.l[r] * exp2((double)st.m[r] - (double)mm);
     ll += __shfl_xor(ll, 16, kWave);
     ll += __shfl_xor(ll, 32, kWave);
-    if (grp == 0) {
-      xm[wave * HALF + nb * 16 + col] = mm;
-      xl[wave * HALF + nb * 16 + col] = ll;
-    }
-  }
-  __syncthreads();
-  if (tid < kLseRows) {
-    const int r = tid % HALF, w0 = 2 * (tid / HALF);   // the row half's two waves
-    const int rho = rb * kLseRows + tid;
-    const float m0 = xm[w0 * HALF + r], m1 = xm[(w0 + 1) * HALF + r];
-    const float M = fmaxf(m0, m1);
-    double L = 0.0;
-    if (m0 != -INFINITY) L += xl[w0 * HALF + r] * exp2((double)m0 - (double)M);
-    if (m1 != -INFINITY) L += xl[(w0 + 1) * HALF + r] * exp2((double)m1 - (double)M);
-    if (rho < R) {
+    const int rho = row0 + r * 16 + col;
+    if (grp == 0 && rho < R) {
       const size_t slot = (size_t)ch * geo.hq * geo.n_text + (size_t)g * R + rho;
-      m_part[slot] = M;
-      l_part[slot] = L;
+      m_part[slot] = mm;
+      l_part[slot] = ll;
     }
   }
 }
@@ -456,7 +365,7 @@ __global__ void col_prep(const float* __restrict__ lse, float factor, int R, int
 }
 
 template <int D>
-__global__ __launch_bounds__(kColThreads, kColOcc) void colscore_mfma(
+__global__ __launch_bounds__(kColThreads, kColOcc * kColWaves / 4) void colscore_mfma(
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, Geo geo,
     const float* __restrict__ lsep, int n_ct, int n_split, float* __restrict__ scores,
     double* __restrict__ part) {
@@ -823,10 +732,10 @@ hipError_t launch_mfma_select(const SelectArgs& a, const Geo& geo, float* lse2, 
     const int n_keys = a.text_start + a.n_text;
     const int n_chunks = (n_keys + kLseChunk - 1) / kLseChunk;
     const int R = geo.G * a.n_text;
-    const int n_rb = (R + kLseRows - 1) / kLseRows;
+    const int n_rb = (R + kLseRowsWg - 1) / kLseRowsWg;
     const int n_items = a.hkv * n_chunks * n_rb;
     const int grid = ((n_items + kXcds - 1) / kXcds) * kXcds;
-    lse_partial_mfma<D><<<grid, 256, 0, st>>>(qt, k, geo, n_chunks, n_rb, m_part, l_part);
+    lse_partial_mfma<D><<<grid, kLseThreads, 0, st>>>(qt, k, geo, n_chunks, n_rb, m_part, l_part);
     const int rows = a.hq * a.n_text;
     lse_finalize<<<(rows + 255) / 256, 256, 0, st>>>(m_part, l_part, n_chunks, rows, lse2);
   }
