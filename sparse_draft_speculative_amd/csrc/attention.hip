@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   constexpr int TILE = 64 * D;                       // elements of one K or V tile
   const int len = lsrc.get();
   constexpr int LPT = 64 * CPR / kDenseThreads;      // copies per thread per tensor per tile
-  __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE];   // [buffer][K, V]
+  __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE + 64 * D];   // [buffer][K, V], Q
 
   const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -290,11 +290,19 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   const int qi = rok ? rho / G : 0;
   const int hh = g * G + (rok ? rho % G : 0);
   const int qpos = len - n_q + qi;
-  bf16x8_t qb[D / 32];
-  load_q_operand<D>(q + ((size_t)qi * hq + hh) * D, rok, grp, qb);
-  // the query operand has landed before any copy is in flight, so the
-  // compiler's own waits never count the copies
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // The row block's 64 query rows go to LDS by direct-to-LDS copies ahead
+  // of the first K/V tiles, so their latency overlaps the tiles' (rows past
+  // Rg re-read row Rg - 1; their results are never stored).
+  uint16_t* qs = smem + kDenseBufs * 2 * TILE;
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int slot = kDenseThreads * u + tid;
+    const int row = slot / CPR, phys = slot % CPR;
+    const int rr = min(rb * 64 + row, Rg - 1);
+    const uint16_t* src = q + ((size_t)(rr / G) * hq + g * G + rr % G) * D +
+                          (Tile<D>::slot_k(row, phys) << 3);
+    dma16(src, lds_addr(qs) + (kDenseThreads * u + 64 * wave) * 16);
+  }
 
   const int ntiles_all = (len + 63) / 64;
   // tiles of this split (none when a device length leaves it past the end)
@@ -320,6 +328,15 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
 #pragma unroll
   for (int b = 0; b < kDenseBufs - 1; ++b)
     dense_issue_tile<D>(kbuf(b), vbuf(b), khd, vhd, tile_key(b), len, tid, wave);
+  // the query rows have landed (the prologue's tile copies may still be in
+  // flight); each wave takes its 16 rows' operand
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kDenseBufs - 1) * LPT));
+  __syncthreads();
+  bf16x8_t qb[D / 32];
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qb[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(
+        qs + Tile<D>::off_k(nbw * 16 + col, (D / 32) * grp + kk)));
   for (int i = 0; i < ntiles; i += kDenseBufs) {
 #pragma unroll
     for (int b = 0; b < kDenseBufs; ++b) {
