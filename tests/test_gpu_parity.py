@@ -241,6 +241,36 @@ def test_select_topk_exact_ties_and_prefix(lib):
             assert idx.cpu().numpy().tolist() == [want] * hkv
 
 
+@pytest.mark.parametrize("hq,hkv,d,prefix,vis_len,n_text,topk", [
+    (4, 4, 128, 0, 100, 1, 7),          # one text row per head, G = 1
+    (8, 2, 128, 5, 1000, 3, 64),        # G = 4, rows < one tile, prefix
+    (7, 1, 128, 64, 2000, 17, 500),     # G = 7, a partial query tile
+    (16, 2, 128, 0, 9000, 20, 1024),    # G = 8, keys over two LSE chunks
+    (28, 4, 128, 3, 777, 41, 777),      # K = vis_len; 287 rows per group
+    (8, 8, 64, 0, 385, 9, 33),          # d = 64, a key block past one workgroup
+    (12, 3, 64, 100, 3000, 30, 300),    # d = 64, prefix, rows past one row block
+])
+def test_select_topk_shapes(lib, hq, hkv, d, prefix, vis_len, n_text, topk):
+    """bf16 selection over shapes that leave partial query tiles, partial key
+    blocks, text rows past a row block, keys over several LSE chunks, a
+    non-visual prefix and row-range splits (small grids use several)."""
+    gen = torch.Generator(device="cpu").manual_seed(hq * 1000 + vis_len + n_text)
+    cap = prefix + vis_len + n_text + 5
+    k = torch.randn(hkv, cap, d, generator=gen).bfloat16()
+    q = torch.randn(hq, n_text, d, generator=gen).bfloat16()
+    text_start = prefix + vis_len
+    say(f"select shape hq={hq} hkv={hkv} d={d} prefix={prefix} vis={vis_len} "
+        f"n_text={n_text} K={topk}")
+    idx, scores = lib.std_select_topk(q.cuda(), k.cuda(), cap, text_start, prefix, vis_len, topk,
+                                      want_scores=True)
+    torch.cuda.synchronize()
+    _, ref_scores = oracle.select_topk(f64(q), f64(k), text_start, prefix, vis_len, topk)
+    rel = np.abs(f64(scores) - ref_scores) / ref_scores
+    say(f"  score rel err max {rel.max():.2e}")
+    assert rel.max() < 1e-4
+    check_topk(idx.cpu().numpy(), ref_scores, topk, prefix, vis_len)
+
+
 def test_select_topk_uses_caller_lse(lib):
     cfg = synth.config("c1")
     lay = layer(cfg)
