@@ -245,6 +245,7 @@ def main():
         ph = None
         if timing:
             ph = {"select_ms": e_sel[0].elapsed_time(e_sel[1]),
+                  "cycle_ms": [a.elapsed_time(d) for a, _, _, d in cyc_ev],
                   "draft_ms": sum(a.elapsed_time(b) for a, b, _, _ in cyc_ev),
                   "verify_ms": sum(b.elapsed_time(c) for _, b, c, _ in cyc_ev),
                   "accept_ms": sum(c.elapsed_time(d) for _, _, c, d in cyc_ev),
@@ -260,7 +261,8 @@ def main():
     wall = time.perf_counter() - t0
     new_tok = sum(r[0] for r in results)
     cycles = sum(r[1] for r in results)
-    ph = {k: sum(r[2][k] for r in results) for k in results[0][2]}
+    cycle_ms = sorted(x for r in results for x in r[2]["cycle_ms"])
+    ph = {k: sum(r[2][k] for r in results) for k in results[0][2] if k != "cycle_ms"}
 
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
@@ -337,12 +339,37 @@ def main():
         "accepted_tokens_per_cycle": round(ph["emitted"] / max(cycles, 1), 3),
         "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
         "dense_only_attn_gbps": round(dense_gbps, 1),
+        "cycle_ms": cycle_stats(cycle_ms),
+        "projection": projection(cycle_ms, G, dense_ms_per_tok),
     }
     if not args.no_toy:
         line["toy_e2e"] = toy_e2e()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cpu_layers, args, cycles / args.steps)
     print(json.dumps(line), flush=True)
+
+
+def cycle_stats(ms):
+    """Median, p10 and p90 of the per-cycle times (draft + verify + accept)."""
+    q = lambda f: ms[min(len(ms) - 1, int(f * (len(ms) - 1) + 0.5))]  # noqa: E731
+    return {"cycles": len(ms), "median": round(q(0.5), 4), "p10": round(q(0.1), 4),
+            "p90": round(q(0.9), 4)}
+
+
+def projection(cycle_ms, gamma, dense_ms_per_tok):
+    """Attention-only decode rate projected from the measured median cycle
+    time: E(alpha) = (1 - alpha^(gamma+1)) / (1 - alpha) tokens per cycle
+    under independent per-token acceptance, for alpha in {0.8, 0.9, 0.95},
+    against dense-only decoding (selection not included)."""
+    t = cycle_ms[len(cycle_ms) // 2]
+    out = {"label": "attention-only, projected", "t_cycle_ms": round(t, 4),
+           "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2)}
+    for a in (0.8, 0.9, 0.95):
+        e = (1 - a ** (gamma + 1)) / (1 - a)
+        out[f"alpha_{a}"] = {"tokens_per_cycle": round(e, 3),
+                             "tokens_per_s": round(e * 1e3 / t, 1),
+                             "speedup_vs_dense": round(e * dense_ms_per_tok / t, 3)}
+    return out
 
 
 def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
