@@ -416,10 +416,10 @@ def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
                        f"{n_new} new tokens, weights N(0, 0.02^2)",
            "selection_ms": round(sel_ms, 3),
            "dense_only_tokens_per_s": round((n_new - 1) / t_dense, 2), "std": {}}
-    for g in gammas:
-        (toks, acc), t_std = timed(lambda: dec.decode_std(first, prompt_len, n_new, idx, 0,
+    def run(sel, g):
+        (toks, acc), t_std = timed(lambda: dec.decode_std(first, prompt_len, n_new, sel, 0,
                                                            n_vis, g))
-        out["std"][f"gamma{g}"] = {
+        return {
             "tokens_per_s": round((n_new - 1) / t_std, 2),
             "speedup_vs_dense": round(t_dense / t_std, 3),
             "accepted_tokens_per_dense_step": round(float(np.mean([a + 1 for a in acc])), 3),
@@ -427,8 +427,22 @@ def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
             "cycles": len(acc),
             "stream_equals_dense": toks == dense,
         }
+
+    for g in gammas:
+        out["std"][f"gamma{g}"] = run(idx, g)
+    # Comparator: the same draft kernel over a static visual set -- the first
+    # STREAM_SINK visual positions and the last topk - STREAM_SINK ones -- in
+    # place of the attention-ranked top-K (sizes are this harness's choice).
+    topk = cfg["topk"]
+    fixed = torch.cat([torch.arange(STREAM_SINK), torch.arange(n_vis - (topk - STREAM_SINK), n_vis)])
+    static = [fixed.to(torch.int32).repeat(cfg["n_kv_heads"], 1).contiguous().cuda()
+              for _ in range(cfg["n_layers"])]
+    out["static_window"] = {"sink": STREAM_SINK, "window": topk - STREAM_SINK,
+                            "std": {f"gamma{g}": run(static, g) for g in gammas}}
     return out
 
+
+STREAM_SINK = 64          # visual positions kept from the start in the static-set comparator
 
 TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "traffic_dense_verify_c4.md")
