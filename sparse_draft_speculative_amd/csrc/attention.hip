@@ -203,7 +203,7 @@ template <int D>
 __device__ __forceinline__ void dense_step(const uint16_t* Ks, const uint16_t* Vs,
                                            const bf16x8_t* qb, int kh, int t0, int len,
                                            int safe_end, int qpos, float c, int col, int grp,
-                                           float& m, float& lsum, floatx4_t* oacc) {
+                                           bool rok, float& m, float& lsum, floatx4_t* oacc) {
   constexpr int KST = D / 32;
   constexpr int DB = D / 16;
   floatx4_t sacc[2];
@@ -246,6 +246,10 @@ __device__ __forceinline__ void dense_step(const uint16_t* Ks, const uint16_t* V
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[j] - msafe);
   lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  // padding rows (never stored) feed zeros to the matrix unit: an MFMA on
+  // zero operands draws less power, and this kernel runs at the power limit
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = rok ? p[j] : 0.f;
   // O^T += V^T P^T over the 32 keys (one MFMA step per 16 output columns)
   uint4 pw;
   pw.x = pack_bf16x2(p[0], p[1]);
@@ -332,11 +336,14 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   // flight); each wave takes its 16 rows' operand
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kDenseBufs - 1) * LPT));
   __syncthreads();
+  // (padding rows take a zero operand: see dense_step)
   bf16x8_t qb[D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    qb[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(
-        qs + Tile<D>::off_k(nbw * 16 + col, (D / 32) * grp + kk)));
+  for (int kk = 0; kk < D / 32; ++kk) {
+    uint4 u = *reinterpret_cast<const uint4*>(qs + Tile<D>::off_k(nbw * 16 + col, (D / 32) * grp + kk));
+    if (!rok) u = make_uint4(0u, 0u, 0u, 0u);
+    qb[kk] = as_bf16x8(u);
+  }
   for (int i = 0; i < ntiles; i += kDenseBufs) {
 #pragma unroll
     for (int b = 0; b < kDenseBufs; ++b) {
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
                             tid, wave);
         if (active)
           dense_step<D>(kbuf(b), vbuf(b), qb, kh, tile_key(i + b), len, safe_end, qpos, c, col,
-                        grp, m, lsum, oacc);
+                        grp, rok, m, lsum, oacc);
       }
     }
   }
