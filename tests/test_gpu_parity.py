@@ -271,16 +271,23 @@ def test_select_topk_shapes(lib, hq, hkv, d, prefix, vis_len, n_text, topk):
     check_topk(idx.cpu().numpy(), ref_scores, topk, prefix, vis_len)
 
 
-def test_select_topk_uses_caller_lse(lib):
-    cfg = synth.config("c1")
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_select_topk_uses_caller_lse(lib, name):
+    """The caller's natural-log row LSE replaces step 1 (fp32 and bf16 paths)."""
+    cfg = synth.config(name)
     lay = layer(cfg)
-    # the natural-log LSE of each text row, from the oracle's definition
+    # the natural-log LSE of each text row (all keys up to its own position)
     qf, kf = f64(lay["q_text"]), f64(lay["k"])
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    n_keys = cfg.text_start + cfg.n_text
+    keypos = np.arange(n_keys)[:, None]
+    rowpos = cfg.text_start + np.arange(cfg.n_text)[None, :]
     lse = np.empty((cfg.n_q_heads, cfg.n_text))
     for h in range(cfg.n_q_heads):
-        for i in range(cfg.n_text):
-            s = (kf[0, : cfg.text_start + i + 1] @ qf[h, i]) / np.sqrt(cfg.head_dim)
-            lse[h, i] = s.max() + np.log(np.exp(s - s.max()).sum())
+        s = (kf[h // G, :n_keys] @ qf[h].T) / np.sqrt(cfg.head_dim)   # [keys][rows]
+        s = np.where(keypos <= rowpos, s, -np.inf)
+        mx = s.max(axis=0)
+        lse[h] = mx + np.log(np.exp(s - mx).sum(axis=0))
     lse_t = torch.from_numpy(lse.astype(np.float32)).cuda()
     idx, scores = lib.std_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
                                       cfg.vis_start, cfg.vis_len, cfg.topk, lse=lse_t,
