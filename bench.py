@@ -31,6 +31,7 @@ query per token, no selection), per-kernel HBM GB/s and % of 8 TB/s.
 
 import argparse
 import json
+import math
 import os
 import re
 import sys
@@ -58,6 +59,8 @@ def parse():
     ap.add_argument("--dense-tokens", type=int, default=8)
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the calls one by one instead of replaying captured phases")
+    ap.add_argument("--no-prefill-lse", action="store_true",
+                    help="skip the selection timing with a caller-supplied row LSE")
     ap.add_argument("--no-toy", action="store_true",
                     help="skip the end-to-end toy decoder measurement")
     return ap.parse_args()
@@ -264,6 +267,35 @@ def main():
     cycle_ms = sorted(x for r in results for x in r[2]["cycle_ms"])
     ph = {k: sum(r[2][k] for r in results) for k in results[0][2] if k != "cycle_ms"}
 
+    # selection with the row normaliser (step 1) supplied by the caller, as
+    # a prefill attention kernel returns it; the LSE itself is computed here
+    # in fp32 torch, outside the timed region
+    sel_prefill = None
+    if not args.no_prefill_lse:
+        lses = [prefill_lse(lay, cfg) for lay in layers]
+        idx2 = [torch.zeros_like(t) for t in idx]
+        sel2 = [sd.prepare_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
+                                       cfg.vis_start, cfg.vis_len, cfg.topk, idx2[l], ws_sel,
+                                       lse=lses[l], stream=st)
+                for l, lay in enumerate(layers)]
+        for c in sel2:                         # warm-up
+            c()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(st):
+            e0.record()
+            for c in sel2:
+                c()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        same = sum(len(set(a.tolist()) & set(b.tolist()))
+                   for x, y in zip(idx, idx2) for a, b in zip(x.cpu(), y.cpu()))
+        sel_prefill = {"ms_per_layer": round(ms / L, 3), "ms_per_request": round(ms, 3),
+                       "idx_overlap_with_full_selection": round(same / (L * cfg.n_kv_heads * cfg.topk), 6),
+                       "note": "step 1 (row LSE) supplied by the caller, as the prefill's "
+                               "attention returns it; steps 2-3 timed"}
+
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
     e0, e1 = ev(), ev()
@@ -340,6 +372,7 @@ def main():
         "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
         "dense_only_attn_gbps": round(dense_gbps, 1),
         "cycle_ms": cycle_stats(cycle_ms),
+        "selection_prefill_lse": sel_prefill,
         "projection": projection(cycle_ms, G, dense_ms_per_tok),
     }
     if not args.no_toy:
@@ -347,6 +380,26 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cpu_layers, args, cycles / args.steps)
     print(json.dumps(line), flush=True)
+
+
+def prefill_lse(lay, cfg):
+    """Natural-log LSE of every text row over the keys it sees (the prompt
+    up to its own position), in fp32 torch: the value a prefill attention
+    kernel returns with its output."""
+    import torch
+    q, k = lay["q_text"].float(), lay["k"].float()
+    hq, n_text, d = q.shape
+    G = hq // k.shape[0]
+    n_keys = cfg.text_start + n_text
+    keypos = torch.arange(n_keys, device=q.device)[:, None]
+    rowpos = cfg.text_start + torch.arange(n_text, device=q.device)[None, :]
+    out = torch.empty(hq, n_text, dtype=torch.float32, device=q.device)
+    for h in range(hq):
+        s = (k[h // G, :n_keys] @ q[h].T) * (1.0 / math.sqrt(d))
+        s.masked_fill_(keypos > rowpos, float("-inf"))
+        out[h] = torch.logsumexp(s, dim=0)
+        del s
+    return out
 
 
 def cycle_stats(ms):
