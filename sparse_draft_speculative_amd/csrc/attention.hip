@@ -49,11 +49,19 @@ struct KeyList {
 // Valid cache length of a call: the host value, or (device-length calls)
 // min(max(*dev + off, 1), max) read when the kernel runs, so a decode loop
 // captured once in a graph sees the length the previous step committed.
+// ptr() never is null (a zero word stands in for a missing device length),
+// so a kernel can load it as a vector load issued with its first memory
+// accesses and apply resolve() where the length is first needed.
+__device__ int32_t kNoDeviceLen = 0;
 struct LenSrc {
   int max;
   const int32_t* dev;
   int off;
   __device__ __forceinline__ int get() const { return dev ? min(max_(*dev + off, 1), max) : max; }
+  __device__ __forceinline__ const int32_t* ptr() const { return dev ? dev : &kNoDeviceLen; }
+  __device__ __forceinline__ int resolve(int d) const {
+    return dev ? min(max_(d + off, 1), max) : max;
+  }
   static __device__ __forceinline__ int max_(int a, int b) { return a > b ? a : b; }
 };
 
@@ -293,7 +301,6 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   const bool rok = rho < Rg;
   const int qi = rok ? rho / G : 0;
   const int hh = g * G + (rok ? rho % G : 0);
-  const int qpos = len - n_q + qi;
   // The row block's 64 query rows go to LDS by direct-to-LDS copies ahead
   // of the first K/V tiles, so their latency overlaps the tiles' (rows past
   // Rg re-read row Rg - 1; their results are never stored).
@@ -308,6 +315,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
     dma16(src, lds_addr(qs) + (kDenseThreads * u + 64 * wave) * 16);
   }
 
+  // (the device length, loaded at entry, is first needed here)
+  const int qpos = len - n_q + qi;
   const int ntiles_all = (len + 63) / 64;
   // tiles of this split (none when a device length leaves it past the end)
   const int ntiles = s < ntiles_all ? (ntiles_all - s + splits - 1) / splits : 0;
@@ -417,7 +426,6 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, LenSrc lsrc,
     int splits, float2* __restrict__ ml, float* __restrict__ o) {
-  const int n_entries = vis_start + topk + max(0, lsrc.get() - vis_end);
   constexpr int EW = kSparseEntriesPerWave;
   constexpr int NKB = EW / 16;
   using TM = TileMath<D, NKB>;
@@ -442,21 +450,34 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   uint16_t* Vs = Ks + REGION;
   int* pw = pos_s + wave * EW;
 
+  // Positions come from the list at the host bound (entries past it re-read
+  // its last row), so the index reads and the row gathers do not wait for
+  // the device length; entries past the actual list are masked below.
   KeyList kl{true, idx + (size_t)g * topk, vis_start, vis_end, topk};
+  const int n_bound = vis_start + topk + max(0, lsrc.max - vis_end);
   const int e0 = s * kSparseChunk + wave * EW;   // first entry of this wave
-  if (lane < EW) {
-    const int e = e0 + lane;
-    pw[lane] = e < n_entries ? kl.pos(e) : -1;
-  }
+  // lane EW fetches the device length beside the index reads.  An opaque
+  // zero lane offset makes it a vector load: a scalar load would be waited
+  // for together with the argument loads (scalar loads complete out of
+  // order), i.e. before anything else is issued.
+  int zero_v;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
+  int len_raw = 0;
+  if (lane == EW) len_raw = lsrc.ptr()[zero_v];
+  if (lane < EW) pw[lane] = kl.pos(min(e0 + lane, n_bound - 1));
+  // The query operand: padding columns (G < 16) read a valid row (head g*G)
+  // unconditionally, so the loads need no merge and stay in flight beside
+  // the index reads; their results are never stored.
   bf16x8_t qb[D / 32];
-  load_q_operand<D>(q + (size_t)h * D, row_ok, grp, qb);
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qb[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(q + (size_t)h * D + (D / 4) * grp + 8 * kk));
   // pw is written and read by this wave only
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
 
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
-  const int last = kl.pos(n_entries - 1);   // a valid row for the padded entries
   // gathered rows load in their natural chunk order (short address path
   // after the index read); the swizzle is applied to the LDS stores
   u32x4_t kreg[NL], vreg[NL];
@@ -464,18 +485,23 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   for (int u = 0; u < NL; ++u) {
     const int cl = lane + 64 * u;
     const int row = cl / CPR, chunk = cl % CPR;
-    int pr = pw[row];
-    pr = pr >= 0 ? pr : last;
-    const size_t base = (size_t)pr * D + (chunk << 3);
+    const size_t base = (size_t)pw[row] * D + (chunk << 3);
     kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base);
     vreg[u] = *reinterpret_cast<const u32x4_t*>(vh + base);
   }
+  // Entries past the actual list read rows the cache need not hold finite
+  // values in: their scores are masked by selects below, and their V rows
+  // are stored as zeros so that 0 * V stays 0 in the PV product.
+  const int len = lsrc.resolve(__builtin_amdgcn_readlane(len_raw, EW));
+  const int n_entries = vis_start + topk + max(0, len - vis_end);
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     const int cl = lane + 64 * u;
     const int row = cl / CPR, chunk = cl % CPR;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4_t*>(Ks + Tile<D>::off_k(row, chunk)) = kreg[u];
-    *reinterpret_cast<u32x4_t*>(Vs + Tile<D>::off_v(row, chunk)) = vreg[u];
+    *reinterpret_cast<u32x4_t*>(Vs + Tile<D>::off_v(row, chunk)) =
+        e0 + row < n_entries ? vreg[u] : zero;
   }
   // the wave reads back only its own region: no workgroup barrier needed
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS stores done
@@ -491,7 +517,8 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     float x[4 * NKB], p[4 * NKB];
 #pragma unroll
     for (int j = 0; j < 4 * NKB; ++j)
-      x[j] = pw[(j >> 2) * 16 + 4 * grp + (j & 3)] >= 0 ? sacc[j >> 2][j & 3] * c : -INFINITY;
+      x[j] = e0 + (j >> 2) * 16 + 4 * grp + (j & 3) < n_entries ? sacc[j >> 2][j & 3] * c
+                                                                 : -INFINITY;
     online_update<DB, 4 * NKB>(x, p, m, lsum, oacc);
     TM::pv(Vs, p, col, grp, oacc);
   }
