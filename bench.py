@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--dense-tokens", type=int, default=8)
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the calls one by one instead of replaying captured phases")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="skip the batched sparse draft measurement")
     ap.add_argument("--no-prefill-lse", action="store_true",
                     help="skip the selection timing with a caller-supplied row LSE")
     ap.add_argument("--no-toy", action="store_true",
@@ -278,6 +280,7 @@ def main():
                                        cfg.vis_start, cfg.vis_len, cfg.topk, idx2[l], ws_sel,
                                        lse=lses[l], stream=st)
                 for l, lay in enumerate(layers)]
+        torch.cuda.synchronize()               # the LSEs come from the current stream
         for c in sel2:                         # warm-up
             c()
         torch.cuda.synchronize()
@@ -295,6 +298,8 @@ def main():
                        "idx_overlap_with_full_selection": round(same / (L * cfg.n_kv_heads * cfg.topk), 6),
                        "note": "step 1 (row LSE) supplied by the caller, as the prefill's "
                                "attention returns it; steps 2-3 timed"}
+
+    batch_sparse = None if args.no_batch else batched_sparse(sd, cfg, layers[0], idx[0], st)
 
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
@@ -373,6 +378,7 @@ def main():
         "dense_only_attn_gbps": round(dense_gbps, 1),
         "cycle_ms": cycle_stats(cycle_ms),
         "selection_prefill_lse": sel_prefill,
+        "batched_sparse": batch_sparse,
         "projection": projection(cycle_ms, G, dense_ms_per_tok),
     }
     if not args.no_toy:
@@ -380,6 +386,50 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cpu_layers, args, cycles / args.steps)
     print(json.dumps(line), flush=True)
+
+
+def batched_sparse(sd, cfg, lay, idx, st, batches=(1, 4, 16), reps=20):
+    """Sparse draft attention of one c4 layer for B independent sequences in
+    one launch (std_sparse_decode_attn_batch; B copies of the layer's cache
+    and index list at distinct addresses), each at length ctx + 1: HBM GB/s
+    against B x the single-sequence algorithmic bytes."""
+    import torch
+    out = {"layer_bytes_per_sequence": int(attn_bytes_sparse(cfg, cfg.ctx + 1))}
+    L = cfg.ctx + 1
+    for B in batches:
+        k = lay["k"][None].expand(B, *lay["k"].shape).contiguous()
+        v = lay["v"][None].expand(B, *lay["v"].shape).contiguous()
+        q = lay["q_draft"][0][None].expand(B, *lay["q_draft"][0].shape).contiguous()
+        ib = idx[None].expand(B, *idx.shape).contiguous()
+        o = torch.empty_like(q)
+        shape = sd.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+        ws = torch.zeros(max(sd.std_sparse_decode_batch_workspace(shape, B, k, L, cfg.vis_start,
+                                                                  cfg.vis_len, cfg.topk), 256),
+                         dtype=torch.uint8, device=q.device)
+
+        # the copies above ran on the current stream, the calls run on st
+        torch.cuda.synchronize()
+
+        def call():
+            sd.std_sparse_decode_attn_batch(q, k, v, L, cfg.vis_start, cfg.vis_len, ib, out=o,
+                                            workspace=ws, stream=st)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(st):
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbps = B * out["layer_bytes_per_sequence"] / (us * 1e-6) / 1e9
+        out[f"batch{B}"] = {"us_per_launch": round(us, 2), "achieved_gbps": round(gbps, 1),
+                            "frac": round(gbps * 1e9 / PEAK_HBM, 4)}
+        del k, v, q, ib, o, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def prefill_lse(lay, cfg):

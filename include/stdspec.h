@@ -32,7 +32,9 @@
  * - Argument checks run on the host before any launch; a failed check returns
  *   a status and launches nothing.  STD_ERR_HIP reports a launch failure.
  *   Device-side contents (idx inside the visual span, ascending, distinct)
- *   are preconditions and are not checked.  Nothing prints or aborts.
+ *   are preconditions and are not checked; an idx entry outside the span is
+ *   clamped into it (the output is then unspecified, but every access stays
+ *   inside the cache).  Nothing prints or aborts.
  * - stream is a hipStream_t passed as void*; NULL means the default stream.
  * - Workspace: each call that needs scratch takes a caller-allocated device
  *   buffer of at least the size its *_workspace query returns (256-byte
@@ -206,6 +208,30 @@ std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* shape, const voi
                                         int32_t n_q, const std_kv_t* kv, const int32_t* len_dev,
                                         int32_t len_offset, void* out, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (b, batched) Sparse draft attention for `batch` independent sequences in
+ * one launch: the draft step of (b) applied to each sequence, data-parallel
+ * over requests (the pages fix no batch size; this serves batch > 1).
+ *
+ * Layout: q and out [batch][n_q_heads][head_dim]; the caches lie back to
+ * back, K and V [batch][n_kv_heads][kv->capacity][head_dim] (kv->k, kv->v
+ * point at sequence 0); idx [batch][n_kv_heads][topk], each list as in (b).
+ * kv->len bounds every sequence's length and sizes the launch; sequence b
+ * uses min(max(len_dev[b] + len_offset, 1), kv->len) when len_dev (batch
+ * int32 in device memory) is given, else kv->len.  All sequences share vis
+ * and topk.  bf16 KV with n_q_heads / n_kv_heads <= 16 only
+ * (STD_ERR_UNSUPPORTED otherwise); 1 <= batch <= 65535.  With batch == 1
+ * the result equals std_sparse_decode_attn(_dlen) bit for bit.
+ * ------------------------------------------------------------------------ */
+size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* shape, int32_t batch,
+                                         const std_kv_t* kv, std_vis_t vis, int32_t topk);
+std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* shape, const void* q,
+                                          int32_t batch, const std_kv_t* kv,
+                                          const int32_t* len_dev, int32_t len_offset,
+                                          std_vis_t vis, const int32_t* idx, int32_t topk,
+                                          void* out, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /* ------------------------------------------------------------------------
  * (d) Greedy acceptance plus the bonus token.

@@ -11,7 +11,8 @@ binding over it (torch supplies device memory and the HIP stream):
 
 std_sparse_decode_attn_dlen / std_dense_verify_attn_dlen read the valid
 cache length from device memory, so a whole draft-verify cycle can be
-captured once and replayed.
+captured once and replayed; std_sparse_decode_attn_batch runs the draft
+step for several independent sequences in one launch.
 
 Importing this package does not load the library; the first call does, and
 fails loudly if it has not been built.
@@ -21,6 +22,7 @@ from ._lib import (  # noqa: F401
     StdError, load, attn_shape, kv_desc,
     std_select_topk, std_select_topk_workspace,
     std_sparse_decode_attn, std_sparse_decode_workspace, std_sparse_decode_attn_dlen,
+    std_sparse_decode_attn_batch, std_sparse_decode_batch_workspace,
     std_dense_verify_attn, std_dense_verify_workspace, std_dense_verify_attn_dlen,
     std_accept,
     PreparedCall, prepare_dense_verify, prepare_sparse_decode, prepare_select_topk,

@@ -64,6 +64,11 @@ _SIGS = {
                                                    _P, _SZ, _P]),
     "std_sparse_decode_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, ctypes.POINTER(KV),
                                               Vis, _P, _I, _P, _P, _SZ, _P]),
+    "std_sparse_decode_batch_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I,
+                                                ctypes.POINTER(KV), Vis, _I]),
+    "std_sparse_decode_attn_batch": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I,
+                                                    ctypes.POINTER(KV), _P, _I, Vis, _P, _I, _P,
+                                                    _P, _SZ, _P]),
     "std_select_topk_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, Vis, _I,
                                         ctypes.POINTER(KV)]),
     "std_select_topk": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
@@ -138,7 +143,7 @@ def kv_desc(k, v, length):
 
 
 def _workspace(nbytes, device, workspace):
-    # zero-filled: the library's ticket counters must start at zero
+    # the library needs no initialised workspace; zero-filled for tidiness
     if workspace is None:
         return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     _dev(workspace, "workspace")
@@ -254,6 +259,54 @@ def std_sparse_decode_attn_dlen(q, k, v, max_len, len_dev, len_offset, vis_start
                                            _ptr(len_dev), int(len_offset), vis, _ptr(idx), topk,
                                            _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "std_sparse_decode_attn_dlen")
+    return out
+
+
+def std_sparse_decode_batch_workspace(shape, batch, k, length, vis_start, vis_len, topk):
+    """Workspace bytes of std_sparse_decode_attn_batch; k [B][H_kv][capacity][d]."""
+    kv = KV(k.data_ptr(), 0, k.shape[2], int(length), _dtype_code(k))
+    return load().std_sparse_decode_batch_workspace(ctypes.byref(shape), int(batch),
+                                                    ctypes.byref(kv), Vis(vis_start, vis_len),
+                                                    int(topk))
+
+
+def std_sparse_decode_attn_batch(q, k, v, max_len, vis_start, vis_len, idx, len_dev=None,
+                                 len_offset=0, out=None, scale=None, workspace=None, stream=None):
+    """Sparse draft attention for B sequences in one launch.
+
+    q [B][H_q][d]; k, v [B][H_kv][capacity][d]; idx [B][H_kv][K] int32;
+    len_dev None (every sequence has length max_len) or [B] int32 device
+    lengths, sequence b using min(max(len_dev[b] + len_offset, 1), max_len).
+    """
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx")):
+        _dev(t, n)
+    if idx.dtype != torch.int32:
+        raise ValueError("idx must be int32")
+    B, hq, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or v.shape != k.shape:
+        raise ValueError("k and v must be [B][H_kv][capacity][d] with the batch of q")
+    hkv, cap = k.shape[1], k.shape[2]
+    if idx.dim() != 3 or idx.shape[0] != B or idx.shape[1] != hkv:
+        raise ValueError("idx must be [B][H_kv][K]")
+    if len_dev is not None:
+        _dev(len_dev, "len_dev")
+        if len_dev.dtype != torch.int32 or len_dev.numel() != B:
+            raise ValueError("len_dev must be [B] int32")
+    topk = idx.shape[2]
+    shape = attn_shape(hq, hkv, d, scale)
+    kv = KV(k.data_ptr(), v.data_ptr(), cap, int(max_len), _dtype_code(k))
+    vis = Vis(vis_start, vis_len)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    ws = _workspace(lib.std_sparse_decode_batch_workspace(ctypes.byref(shape), B,
+                                                          ctypes.byref(kv), vis, topk),
+                    q.device, workspace)
+    _check(lib.std_sparse_decode_attn_batch(ctypes.byref(shape), _ptr(q), B, ctypes.byref(kv),
+                                            _ptr(len_dev), int(len_offset), vis, _ptr(idx), topk,
+                                            _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "std_sparse_decode_attn_batch")
     return out
 
 

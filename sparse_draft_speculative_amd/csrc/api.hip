@@ -205,9 +205,9 @@ size_t std_sparse_decode_workspace(const std_attn_shape_t* s, const std_kv_t* kv
 
 namespace {
 
-std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
-                           const int32_t* len_dev, int32_t len_off, std_vis_t vis,
-                           const int32_t* idx, int32_t topk, void* out, void* ws,
+std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t batch,
+                           const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
+                           std_vis_t vis, const int32_t* idx, int32_t topk, void* out, void* ws,
                            size_t ws_bytes, void* stream) {
   TRY(check_shape(s));
   TRY(check_kv(kv, true));
@@ -217,13 +217,20 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, const std_k
   CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
   CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
         STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
+  CHECK(batch >= 1 && batch <= 65535 && (long long)batch * s->n_q_heads <= (1 << 24),
+        STD_ERR_INVALID_ARGUMENT, "need 1 <= batch (%d) <= 65535 and batch * n_q_heads <= 2^24",
+        batch);
+  if (batch > 1) {
+    CHECK(kv->dtype == STD_DTYPE_BF16 && s->n_q_heads / s->n_kv_heads <= 16,
+          STD_ERR_UNSUPPORTED, "batched sparse decode needs bf16 KV and G <= 16");
+  }
   const int splits = sparse_splits(kv, vis, topk);
-  const SplitWorkspace w = split_workspace(splits, s->n_q_heads, s->head_dim);
+  const SplitWorkspace w = split_workspace(splits, batch * s->n_q_heads, s->head_dim);
   TRY(check_ws(ws, ws_bytes, w.bytes()));
   AttnArgs a{};
   a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
-  a.capacity = kv->capacity; a.len = kv->len; a.n_q = 1;
+  a.capacity = kv->capacity; a.len = kv->len; a.n_q = batch; a.batch = batch;
   a.len_dev = len_dev; a.len_off = len_off;
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = true; a.idx = idx;
@@ -241,7 +248,7 @@ extern "C" {
 std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
                                     std_vis_t vis, const int32_t* idx, int32_t topk, void* out,
                                     void* ws, size_t ws_bytes, void* stream) {
-  return sparse_decode(s, q, kv, nullptr, 0, vis, idx, topk, out, ws, ws_bytes, stream);
+  return sparse_decode(s, q, 1, kv, nullptr, 0, vis, idx, topk, out, ws, ws_bytes, stream);
 }
 
 std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* q,
@@ -250,7 +257,26 @@ std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* 
                                          int32_t topk, void* out, void* ws, size_t ws_bytes,
                                          void* stream) {
   CHECK(len_dev, STD_ERR_INVALID_ARGUMENT, "len_dev is null");
-  return sparse_decode(s, q, kv, len_dev, len_offset, vis, idx, topk, out, ws, ws_bytes, stream);
+  return sparse_decode(s, q, 1, kv, len_dev, len_offset, vis, idx, topk, out, ws, ws_bytes,
+                       stream);
+}
+
+size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* s, int32_t batch,
+                                         const std_kv_t* kv, std_vis_t vis, int32_t topk) {
+  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK ||
+      check_sparse(s, kv, vis, topk) != STD_OK || batch < 1 || batch > 65535)
+    return 0;
+  return split_workspace(sparse_splits(kv, vis, topk), batch * s->n_q_heads, s->head_dim)
+      .bytes();
+}
+
+std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* s, const void* q,
+                                          int32_t batch, const std_kv_t* kv,
+                                          const int32_t* len_dev, int32_t len_offset,
+                                          std_vis_t vis, const int32_t* idx, int32_t topk,
+                                          void* out, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_decode(s, q, batch, kv, len_dev, len_offset, vis, idx, topk, out, ws, ws_bytes,
+                       stream);
 }
 
 // ---------------------------------------------------------------- selection

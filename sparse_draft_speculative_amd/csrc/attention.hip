@@ -35,6 +35,8 @@ namespace stdspec {
 namespace {
 
 // Entry e of the key list of one KV head -> cache position.
+// A selected position outside the visual span is clamped into it: the
+// result for such a list is unspecified, but no access leaves the cache.
 struct KeyList {
   bool sparse;
   const int32_t* idx;   // this head's selected positions (sparse only)
@@ -42,7 +44,7 @@ struct KeyList {
   __device__ __forceinline__ int pos(int e) const {
     if (!sparse || e < vis_start) return e;
     const int t = e - vis_start;
-    return t < topk ? idx[t] : vis_end + (t - topk);
+    return t < topk ? min(max(idx[t], vis_start), vis_end - 1) : vis_end + (t - topk);
   }
 };
 
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, LenSrc lsrc,
-    int splits, float2* __restrict__ ml, float* __restrict__ o) {
+    int splits, int rows_total, float2* __restrict__ ml, float* __restrict__ o) {
   constexpr int EW = kSparseEntriesPerWave;
   constexpr int NKB = EW / 16;
   using TM = TileMath<D, NKB>;
@@ -440,7 +442,13 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   __shared__ int pos_s[kSparseChunk];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
-  const int s = blockIdx.x, g = blockIdx.y;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;   // split, KV head, sequence
+  // sequence b of a batch: its query rows, cache, index list and length
+  q += (size_t)b * hq * D;
+  k += (size_t)b * hkv * capacity * D;
+  v += (size_t)b * hkv * capacity * D;
+  idx += (size_t)b * hkv * topk;
+  if (lsrc.dev) lsrc.dev += b;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = hq / hkv;
   const int col = lane & 15, grp = lane >> 4;
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
         for (int i = 0; i < 4; ++i) acc[db][i] = fmaf(src[2 + 4 * db + i], a, acc[db][i]);
     }
     if (row_ok) {
-      const size_t slot = (size_t)s * hq + h;
+      const size_t slot = (size_t)s * rows_total + (size_t)b * hq + h;
       if (grp == 0) ml[slot] = make_float2(M, L);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -752,9 +760,10 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   const LenSrc lsrc{a.len, a.len_dev, a.len_off};
   if (a.sparse) {
-    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv), 64 * kSparseWaves, 0, st>>>(
+    const int batch = a.batch > 1 ? a.batch : 1;
+    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv, batch), 64 * kSparseWaves, 0, st>>>(
         q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
-        a.topk, lsrc, a.splits, reinterpret_cast<float2*>(a.ml), a.o);
+        a.topk, lsrc, a.splits, batch * a.hq, reinterpret_cast<float2*>(a.ml), a.o);
   } else {
     const int rows_group = a.n_q * (a.hq / a.hkv);
     dim3 grid(a.splits, a.hkv, (rows_group + 63) / 64);

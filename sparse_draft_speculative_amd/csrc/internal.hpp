@@ -71,8 +71,12 @@ struct AttnArgs {
   float scale;
   int capacity, len, n_q;
   // device-resident length (null: use len); valid length min(*len_dev + len_off, len)
+  // (sparse batch: len_dev[b] for sequence b)
   const int32_t* len_dev;
   int len_off;
+  // sparse only: independent sequences laid out back to back (q, out
+  // [batch][Hq][D], K and V [batch][Hkv][capacity][D], idx [batch][Hkv][topk])
+  int batch;
   bool bf16;
   // sparse key list; for dense, sparse == false
   bool sparse;

@@ -127,6 +127,39 @@ def test_device_length_calls_reject():
     assert sparse() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_batched_sparse_decode_rejects():
+    """The batched draft call: batch in [1, 65535], bf16 with G <= 16, and
+    the host checks of the single-sequence call."""
+    lib = _lib.load()
+    sh = _shape()
+    P = ctypes.c_void_p
+
+    def call(batch=4, kv=None, topk=64, len_dev=0):
+        kv = kv or _kv()
+        return lib.std_sparse_decode_attn_batch(ctypes.byref(sh), P(FAKE), batch,
+                                                ctypes.byref(kv), P(len_dev), 0,
+                                                _lib.Vis(0, 800), P(FAKE), topk, P(FAKE), None, 0,
+                                                None)
+
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    assert call(batch=0) == E
+    assert call(batch=65536) == E
+    assert call(topk=801) == E
+    assert call(kv=_kv(dtype=_lib.STD_DTYPE_F32)) == _lib.STD_ERR_UNSUPPORTED
+    assert call() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert call(len_dev=FAKE) == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert call(batch=1, kv=_kv(dtype=_lib.STD_DTYPE_F32)) == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    one = lib.std_sparse_decode_batch_workspace(ctypes.byref(sh), 1, ctypes.byref(_kv()),
+                                                _lib.Vis(0, 800), 64)
+    four = lib.std_sparse_decode_batch_workspace(ctypes.byref(sh), 4, ctypes.byref(_kv()),
+                                                 _lib.Vis(0, 800), 64)
+    single = lib.std_sparse_decode_workspace(ctypes.byref(sh), ctypes.byref(_kv()),
+                                             _lib.Vis(0, 800), 64)
+    assert one == single and four > one
+    assert lib.std_sparse_decode_batch_workspace(ctypes.byref(sh), 0, ctypes.byref(_kv()),
+                                                 _lib.Vis(0, 800), 64) == 0
+
+
 def test_select_rejects():
     lib = _lib.load()
     sh = _shape()

@@ -345,3 +345,37 @@ def test_sparse_decode_reuses_one_workspace(lib):
             ref = oracle.sparse_decode(f64(q), kf, vf, length, cfg.vis_start, cfg.vis_len,
                                        idx_ref[:, : cfg.topk - 100 * rep])
             assert max_abs(f64(out), ref) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_sparse_decode_clamps_out_of_span_positions(lib, name):
+    """A selected position outside the visual span is read as the nearest end
+    of the span: a malformed list never leaves the cache.  The two
+    out-of-span values here (3 below, 2 above the span) lie inside the cache,
+    and the result must match the clamped list, not the raw one."""
+    cfg = synth.config(name)
+    lay = layer(cfg)
+    vs, vl = 16, cfg.vis_len - 16
+    ve, length, topk = vs + vl, cfg.draft_len(0), 64
+    rng = np.random.default_rng(7)
+    raw, clamped = [], []
+    for _ in range(cfg.n_kv_heads):
+        mid = np.sort(rng.choice(np.arange(vs + 1, ve - 1), topk - 2, replace=False))
+        raw.append(np.concatenate([[vs - 3], mid, [ve + 2]]))
+        clamped.append(np.concatenate([[vs], mid, [ve - 1]]))
+    idx = torch.tensor(np.array(raw), dtype=torch.int32, device="cuda")
+    q = lay["q_draft"][0].contiguous()
+    say(f"sparse clamp {name} len={length} span=[{vs},{ve}) K={topk}")
+    out = f64(lib.std_sparse_decode_attn(q, lay["k"], lay["v"], length, vs, vl, idx))
+    torch.cuda.synchronize()
+    qf, kf, vf = f64(q), f64(lay["k"]), f64(lay["v"])
+    ref = oracle.sparse_decode(qf, kf, vf, length, vs, vl, np.array(clamped))
+    # the raw list read literally (its two rows duplicate prefix/tail keys)
+    G, scale = cfg.n_q_heads // cfg.n_kv_heads, 1.0 / np.sqrt(cfg.head_dim)
+    ref_raw = np.empty_like(ref)
+    for g in range(cfg.n_kv_heads):
+        keys = np.concatenate([np.arange(0, vs), raw[g], np.arange(ve, length)])
+        for h in range(g * G, (g + 1) * G):
+            ref_raw[h] = oracle.attend(qf[h], kf[g, keys], vf[g, keys], scale)
+    assert max_abs(ref, ref_raw) > 2 * TOL[cfg.dtype]      # the case discriminates
+    assert max_abs(out, ref) <= TOL[cfg.dtype]
