@@ -323,10 +323,13 @@ def main():
     sel_ms_layer = ph["select_ms"] / (args.steps * L)
     sel_tflops = select_flops(cfg) / (sel_ms_layer * 1e-3) / 1e12
 
+    probe = read_probe(sd, attn_bytes_dense(cfg, cfg.verify_len, G + 1))
+
     def hbm_roof(gbps, bytes_per_launch):
         return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(gbps * 1e9 / PEAK_HBM, 4),
-                "traffic": None, "bytes_per_launch": int(bytes_per_launch)}
+                "traffic": None, "bytes_per_launch": int(bytes_per_launch),
+                "frac_of_attainable": round(gbps / probe["gbps"], 4)}
 
     dense_roof = hbm_roof(dv_gbps, attn_bytes_dense(cfg, cfg.verify_len, G + 1))
     dense_roof.update(kernel="dense verify (std_dense_verify_attn)",
@@ -379,6 +382,7 @@ def main():
         "cycle_ms": cycle_stats(cycle_ms),
         "selection_prefill_lse": sel_prefill,
         "batched_sparse": batch_sparse,
+        "hbm_read_probe": probe,
         "projection": projection(cycle_ms, G, dense_ms_per_tok),
     }
     if not args.no_toy:
@@ -386,6 +390,34 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cpu_layers, args, cycles / args.steps)
     print(json.dumps(line), flush=True)
+
+
+def read_probe(sd, nbytes, regions=4, reps=40):
+    """Attainable HBM read bandwidth: std_hbm_read_probe (a plain streaming
+    read, one workgroup per CU) over `regions` distinct buffers of the dense
+    verify call's size, launched round-robin so that together they exceed
+    the 256 MB last-level cache and no launch is served from it."""
+    import torch
+    nbytes = int(nbytes) // 16384 * 16384
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(regions)]
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        sd.std_hbm_read_probe(b, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        sd.std_hbm_read_probe(bufs[r % regions], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"gbps": round(gbps, 1), "us_per_launch": round(us, 2), "bytes_per_launch": nbytes,
+            "frac_of_peak": round(gbps * 1e9 / PEAK_HBM, 4),
+            "note": "plain streaming read, 256 workgroups x 256 lanes, 16 KB tiles, "
+                    f"{regions} buffers round-robin"}
 
 
 def batched_sparse(sd, cfg, lay, idx, st, batches=(1, 4, 16), reps=20):

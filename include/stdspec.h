@@ -259,6 +259,46 @@ std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
                         int32_t* n_out, float* margins_or_null,
                         int32_t* seq_len_inout_or_null, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Index-list check (debug aid for (b)).
+ *
+ * The sparse draft calls take, per KV head, selected visual positions
+ * (Technical summary, Methodology item 4: top-K over the visual KV) inside
+ * the span, ascending, without repeats, and do not verify this on the
+ * device (they clamp each position into the span).  This call counts the
+ * entries of idx [n_kv_heads][topk] (int32 device) that lie outside
+ * [vis_start, vis_start + vis_len) or are not larger than the previous
+ * entry of the same head, and writes the count to bad_out (int32 device
+ * scalar; 0 = the list meets every precondition).  topk = 0 writes 0.
+ * Errors: STD_ERR_INVALID_ARGUMENT before any launch for a null pointer,
+ * n_kv_heads < 1, a bad span or topk outside [0, vis_len].
+ * ------------------------------------------------------------------------ */
+std_status_t std_check_idx(const int32_t* idx, int32_t n_kv_heads, int32_t topk, std_vis_t vis,
+                           int32_t* bad_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Streaming-read probe (measurement harness; no step of the method).
+ *
+ * The sparse draft and dense verify calls are bound by HBM bandwidth
+ * (Technical summary, Methodology item 2: the sparse mode cuts draft-phase
+ * I/O; the verify pass reads the full cache once).  This call reads
+ * [buf, buf + bytes) once with a fixed grid of 256 workgroups x 256 lanes
+ * in 16 KB tiles (tile t to workgroup t mod 256) and does nothing else, so
+ * timing it on a buffer larger than the 256 MB last-level cache gives the
+ * read bandwidth this part attains, the yardstick beside the nominal peak.
+ *
+ * buf    device, 16-byte aligned; bytes a positive multiple of 16.
+ * sink   [STD_PROBE_SINK_WORDS] uint32 device, 4-byte aligned: lane l of
+ *        workgroup w writes word 256 w + l, the XOR of every 32-bit word
+ *        it loaded (16-byte element e belongs to tile e / 1024, load
+ *        (e mod 1024) / 256, lane e mod 256).  The digest only keeps the
+ *        loads alive; tests use it to check that every byte was read once.
+ * Errors: STD_ERR_INVALID_ARGUMENT for a null pointer, misalignment or a
+ * bad size, before any launch.
+ * ------------------------------------------------------------------------ */
+#define STD_PROBE_SINK_WORDS 65536
+std_status_t std_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

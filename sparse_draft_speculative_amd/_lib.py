@@ -74,7 +74,11 @@ _SIGS = {
     "std_select_topk": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
                                        ctypes.POINTER(KV), Vis, _I, _P, _P, _P, _P, _SZ, _P]),
     "std_accept": (ctypes.c_int, [_P, _I, _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]),
+    "std_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "std_check_idx": (ctypes.c_int, [_P, _I, _I, Vis, _P, _P]),
 }
+
+PROBE_SINK_WORDS = 65536
 
 _lib = None
 
@@ -367,6 +371,40 @@ def std_accept(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len
                           _stream(stream)),
            "std_accept")
     return out_tokens, n_out
+
+
+def std_check_idx(idx, vis_start, vis_len, bad_out=None, stream=None):
+    """Count the entries of idx [H_kv][K] int32 (device) outside the visual
+    span or not above the previous entry of their head.  Returns the count
+    as a [1] int32 device tensor (0: the list meets every precondition)."""
+    lib = load()
+    _dev(idx, "idx")
+    if idx.dtype != torch.int32 or idx.dim() != 2:
+        raise ValueError("idx must be [H_kv][K] int32")
+    if bad_out is None:
+        bad_out = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _dev(bad_out, "bad_out")
+    _check(lib.std_check_idx(_ptr(idx), idx.shape[0], idx.shape[1], Vis(vis_start, vis_len),
+                             _ptr(bad_out), _stream(stream)),
+           "std_check_idx")
+    return bad_out
+
+
+def std_hbm_read_probe(buf, sink=None, stream=None):
+    """Streaming-read probe: read every byte of the device tensor ``buf``
+    once (size a multiple of 16 bytes).  Returns the [65536] int32 digest
+    (the bit patterns of the C call's uint32 words)."""
+    lib = load()
+    _dev(buf, "buf")
+    if sink is None:
+        sink = torch.empty(PROBE_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < 4 * PROBE_SINK_WORDS:
+        raise ValueError(f"sink must hold {PROBE_SINK_WORDS} 32-bit words")
+    _check(lib.std_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                  _stream(stream)),
+           "std_hbm_read_probe")
+    return sink
 
 
 # ----------------------------------------------------------------------------

@@ -115,6 +115,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
+namespace stdspec {
+// Streaming-read probe (probe.hip): STD_PROBE_SINK_WORDS / 256 workgroups.
+hipError_t launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                                 hipStream_t stream);
+// Index-list check (check.hip): one workgroup.
+hipError_t launch_check_idx(const int32_t* idx, int n_kv_heads, int topk, int vis_start,
+                            int vis_len, int32_t* bad_out, hipStream_t stream);
+}  // namespace stdspec
+
 extern "C" {
 
 int32_t std_abi_version(void) { return STD_ABI_VERSION; }
@@ -350,6 +359,33 @@ std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
   return hip_status(launch_accept(draft, gamma, logits, vocab, logits_dtype == STD_DTYPE_BF16,
                                   out_tokens, n_out, margins_or_null, seq_len_inout_or_null,
                                   static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------ index check
+
+std_status_t std_check_idx(const int32_t* idx, int32_t n_kv_heads, int32_t topk, std_vis_t vis,
+                           int32_t* bad_out, void* stream) {
+  CHECK(bad_out, STD_ERR_INVALID_ARGUMENT, "bad_out is null");
+  CHECK(n_kv_heads >= 1, STD_ERR_INVALID_ARGUMENT, "n_kv_heads must be >= 1");
+  CHECK(vis.vis_start >= 0 && vis.vis_len >= 1 &&
+            (long long)vis.vis_start + vis.vis_len <= 0x7fffffffLL,
+        STD_ERR_INVALID_ARGUMENT, "bad visual span [%d, +%d)", vis.vis_start, vis.vis_len);
+  CHECK(topk >= 0 && topk <= vis.vis_len, STD_ERR_INVALID_ARGUMENT,
+        "need 0 <= topk (%d) <= vis_len (%d)", topk, vis.vis_len);
+  CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
+  return hip_status(launch_check_idx(idx, n_kv_heads, topk, vis.vis_start, vis.vis_len, bad_out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------ read probe
+
+std_status_t std_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  CHECK(buf && sink, STD_ERR_INVALID_ARGUMENT, "buf / sink is null");
+  CHECK(bytes >= 16 && bytes % 16 == 0, STD_ERR_INVALID_ARGUMENT,
+        "bytes (%zu) must be a positive multiple of 16", bytes);
+  CHECK(aligned16(buf) && ((uintptr_t)sink & 3) == 0, STD_ERR_INVALID_ARGUMENT,
+        "buf must be 16-byte aligned and sink 4-byte aligned");
+  return hip_status(launch_hbm_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

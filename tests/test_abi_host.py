@@ -190,6 +190,32 @@ def test_accept_rejects():
     assert lib.std_accept(p, 3, p, 10, 5, p, p, None, None, None) == E
 
 
+def test_check_idx_rejects():
+    lib = _lib.load()
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    p = ctypes.c_void_p(FAKE)
+    vis = _lib.Vis(0, 100)
+    assert lib.std_check_idx(p, 4, 10, vis, None, None) == E
+    assert lib.std_check_idx(None, 4, 10, vis, p, None) == E
+    assert lib.std_check_idx(p, 0, 10, vis, p, None) == E
+    assert lib.std_check_idx(p, 4, -1, vis, p, None) == E
+    assert lib.std_check_idx(p, 4, 101, vis, p, None) == E
+    assert lib.std_check_idx(p, 4, 10, _lib.Vis(-1, 100), p, None) == E
+    assert lib.std_check_idx(p, 4, 10, _lib.Vis(0, 0), p, None) == E
+
+
+def test_read_probe_rejects():
+    lib = _lib.load()
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    p = ctypes.c_void_p(FAKE)
+    assert lib.std_hbm_read_probe(None, 1 << 20, p, None) == E
+    assert lib.std_hbm_read_probe(p, 1 << 20, None, None) == E
+    assert lib.std_hbm_read_probe(p, 0, p, None) == E
+    assert lib.std_hbm_read_probe(p, 17, p, None) == E
+    assert lib.std_hbm_read_probe(ctypes.c_void_p(FAKE + 8), 1 << 20, p, None) == E
+    assert lib.std_hbm_read_probe(p, 1 << 20, ctypes.c_void_p(FAKE + 2), None) == E
+
+
 def test_workspace_sizes():
     lib = _lib.load()
     sh = _shape()
