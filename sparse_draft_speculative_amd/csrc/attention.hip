@@ -173,18 +173,18 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, bool ok, in
 
 // ---------------------------------------------------------------------------
 // Dense verify: grid (split, KV head, 64-row block), 512 threads = 8 waves,
-// one workgroup per CU.
+// at most one workgroup per CU.
 //
 // The len keys form ceil(len/64) tiles of 64; split s takes tiles s,
 // s + S, s + 2S, ... (S splits, a function of len and H_kv only), so at any
 // moment the workgroups of a head sweep one contiguous region of the cache.
 // K and V tiles move global -> LDS by direct-to-LDS copies (no staging
-// registers) into four buffers, three tiles in flight.  Wave w reduces key
+// registers) into three buffers, two tiles in flight.  Wave w reduces key
 // half w & 1 of every tile for the 16 query rows of block w >> 1; the two
 // key halves are merged in LDS at the end.  Every K/V byte is read from HBM
 // once per call when n_q * G <= 64.
 constexpr int kDenseThreads = 512;
-constexpr int kDenseBufs = 4;
+constexpr int kDenseBufs = 3;
 
 // Copy one 64-key tile of K and V (rows past the end re-read row len - 1)
 // into the swizzled LDS layout of Tile<D>.  Thread tid fills 16-byte slots
@@ -334,12 +334,12 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Step i: wait until tile i has landed (tiles i+1, i+2 may still be in
-  // flight), barrier, refill the buffer read in step i-1 with tile i+3,
-  // reduce tile i.  Copies past the last tile re-read valid rows, so the
-  // count in flight is the same at every step.  Unrolled by four so every
-  // buffer index is static.
-  constexpr int kInFlight = 2 * (kDenseBufs - 2) * LPT;   // copies of two tiles
+  // Step i (B = kDenseBufs buffers): wait until tile i has landed (tiles
+  // i+1 .. i+B-2 may still be in flight), barrier, refill the buffer read
+  // in step i-1 with tile i+B-1, reduce tile i.  Copies past the last tile
+  // re-read valid rows, so the count in flight is the same at every step.
+  // Unrolled by B so every buffer index is static.
+  constexpr int kInFlight = 2 * (kDenseBufs - 2) * LPT;   // copies of B-2 tiles
 #pragma unroll
   for (int b = 0; b < kDenseBufs - 1; ++b)
     dense_issue_tile<D>(kbuf(b), vbuf(b), khd, vhd, tile_key(b), len, tid, wave);
