@@ -104,6 +104,8 @@ def test_dense_single_query_decode(lib, name):
     (4, 4, 64, "f32", 3, 777, 800),         # G = 1, fp32
     (32, 1, 128, "bf16", 5, 4097, 4100),    # G = 32
     (6, 2, 128, "f32", 2, 130, 130),
+    (4, 1, 64, "f32", 1, 1, 1),             # one key: the output is that key's V row
+    (28, 4, 128, "bf16", 1, 1, 8),          # one valid key in a larger cache
 ])
 def test_dense_verify_shapes(lib, hq, hkv, d, dtype, n_q, length, cap):
     g = torch.Generator(device="cuda").manual_seed(hq * 1000 + length)
@@ -176,6 +178,8 @@ def test_sparse_full_selection_equals_dense(lib, name):
     (34, 2, 128, "bf16", 0, 1000, 1100, 100),       # G = 17: vector-ALU path
     (4, 1, 64, "f32", 10, 1000, 1200, 77),
     (7, 7, 128, "f32", 0, 300, 301, 300),           # G = 1, K = vis_len
+    (4, 2, 128, "bf16", 0, 1, 5, 1),                # one-position visual span
+    (4, 2, 64, "f32", 3, 1, 9, 1),                  # one-position span after a prefix
 ])
 def test_sparse_decode_shapes(lib, hq, hkv, d, dtype, prefix, vis_len, length, topk):
     gen = torch.Generator(device="cpu").manual_seed(hq * 7 + topk)
@@ -249,6 +253,8 @@ def test_select_topk_exact_ties_and_prefix(lib):
     (28, 4, 128, 3, 777, 41, 777),      # K = vis_len; 287 rows per group
     (8, 8, 64, 0, 385, 9, 33),          # d = 64, a key block past one workgroup
     (12, 3, 64, 100, 3000, 30, 300),    # d = 64, prefix, rows past one row block
+    (4, 1, 128, 0, 1, 4, 1),            # one-position visual span, K = 1
+    (8, 2, 64, 2, 1, 3, 1),             # the same after a prefix, d = 64
 ])
 def test_select_topk_shapes(lib, hq, hkv, d, prefix, vis_len, n_text, topk):
     """bf16 selection over shapes that leave partial query tiles, partial key
