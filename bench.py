@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--dense-tokens", type=int, default=8)
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the calls one by one instead of replaying captured phases")
+    ap.add_argument("--sel-streams", type=int, default=2,
+                    help="streams the per-layer selections are dealt over")
     ap.add_argument("--no-batch", action="store_true",
                     help="skip the batched sparse draft measurement")
     ap.add_argument("--no-prefill-lse", action="store_true",
@@ -138,10 +140,32 @@ def main():
     # one by one instead).
     st = torch.cuda.Stream()
     seq = torch.zeros(1, dtype=torch.int32, device=dev)
+    # Selection deals layers round-robin over --sel-streams streams (each
+    # with its own workspace), so one layer's tail kernels (top-K runs one
+    # workgroup per KV head) and the big kernels' last partial rounds
+    # overlap the next layer's passes.
+    nss = max(1, args.sel_streams)
+    st_sel = [st] + [torch.cuda.Stream() for _ in range(nss - 1)]
+    ws_sels = [ws_sel] + [torch.zeros_like(ws_sel) for _ in range(nss - 1)]
     sel_calls = [sd.prepare_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
-                                        cfg.vis_start, cfg.vis_len, cfg.topk, idx[l], ws_sel,
-                                        stream=st)
+                                        cfg.vis_start, cfg.vis_len, cfg.topk, idx[l],
+                                        ws_sels[l % nss], stream=st_sel[l % nss])
                  for l, lay in enumerate(layers)]
+
+    def select_all():
+        """The 28 selections, enqueued on st; the other streams join st
+        before and after (their calls overwrite index lists that the previous
+        request's draft steps read, and the draft steps read their output)."""
+        fork = torch.cuda.Event()
+        fork.record(st)
+        for x in st_sel[1:]:
+            x.wait_event(fork)
+        for c in sel_calls:
+            c()
+        for x in st_sel[1:]:
+            join = torch.cuda.Event()
+            join.record(x)
+            st.wait_event(join)
     q_draft = [[lay["q_draft"][j].contiguous() for j in range(G)] for lay in layers]
     sp_calls = [[sd.prepare_sparse_decode_dlen(q_draft[l][j], lay["k"], lay["v"], cfg.vis_start,
                                                cfg.vis_len, idx[l], out_sp, ws_sparse, seq, 1 + j,
@@ -220,8 +244,7 @@ def main():
         cyc_ev = []
         with torch.cuda.stream(st):
             e_sel[0].record()
-            for c in sel_calls:
-                c()
+            select_all()
             e_sel[1].record()
             seq.fill_(cfg.ctx)
             t = cfg.ctx
