@@ -152,7 +152,7 @@ def main():
                                         ws_sels[l % nss], stream=st_sel[l % nss])
                  for l, lay in enumerate(layers)]
 
-    def select_all():
+    def select_all(calls=sel_calls):
         """The 28 selections, enqueued on st; the other streams join st
         before and after (their calls overwrite index lists that the previous
         request's draft steps read, and the draft steps read their output)."""
@@ -160,7 +160,7 @@ def main():
         fork.record(st)
         for x in st_sel[1:]:
             x.wait_event(fork)
-        for c in sel_calls:
+        for c in calls:
             c()
         for x in st_sel[1:]:
             join = torch.cuda.Event()
@@ -300,18 +300,16 @@ def main():
         lses = [prefill_lse(lay, cfg) for lay in layers]
         idx2 = [torch.zeros_like(t) for t in idx]
         sel2 = [sd.prepare_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
-                                       cfg.vis_start, cfg.vis_len, cfg.topk, idx2[l], ws_sel,
-                                       lse=lses[l], stream=st)
+                                       cfg.vis_start, cfg.vis_len, cfg.topk, idx2[l],
+                                       ws_sels[l % nss], lse=lses[l], stream=st_sel[l % nss])
                 for l, lay in enumerate(layers)]
         torch.cuda.synchronize()               # the LSEs come from the current stream
-        for c in sel2:                         # warm-up
-            c()
+        select_all(sel2)                       # warm-up
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
         with torch.cuda.stream(st):
             e0.record()
-            for c in sel2:
-                c()
+            select_all(sel2)
             e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
