@@ -19,7 +19,11 @@ float64, slow and direct, so it can be checked against the pages by eye:
                        summary, Methodology item 2, sparse model M_s).
 * ``dense_verify``  -- the dense model's causal attention for the gamma+1
                        verification queries (Methodology item 2, dense model
-                       M; item 3, verification).
+                       M; item 3, verification); the same function gives
+                       the prefill attention of the text rows.
+* ``row_lse``       -- the log softmax normaliser of each of those rows (what
+                       a prefill attention returns beside its output for the
+                       selection's first step, Methodology item 4).
 * ``accept``        -- greedy longest-prefix acceptance plus the bonus token
                        (Methodology item 3, decoding procedure).
 * ``toy``           -- a tiny float64 decoder that runs plain greedy decoding
@@ -33,12 +37,12 @@ invariants, the sparse==dense special case, an independent library routine
 the acceptance rule and the losslessness invariant of the toy loop.
 """
 
-from .attention import dense_verify, sparse_decode, sparse_key_set, attend
+from .attention import dense_verify, sparse_decode, sparse_key_set, attend, row_lse
 from .selection import select_topk, selection_scores, rank_topk
 from .acceptance import accept, argmax_margin
 
 __all__ = [
-    "dense_verify", "sparse_decode", "sparse_key_set", "attend",
+    "dense_verify", "sparse_decode", "sparse_key_set", "attend", "row_lse",
     "select_topk", "selection_scores", "rank_topk",
     "accept", "argmax_margin",
 ]

@@ -65,6 +65,38 @@ def dense_verify(q, k, v, length, scale=None):
     return out
 
 
+def row_lse(q, k, length, scale=None):
+    """Natural-log softmax normaliser of every query row of ``dense_verify``.
+
+    Query i of n_q (position length - n_q + i) of head h has
+    lse = log sum_{j <= position} exp(scale * q.k_j), the log of the
+    denominator of its causal softmax: the value a prefill attention returns
+    beside its output, which the selection's first step (the text rows'
+    normalisers; technical summary, Methodology item 4) then need not
+    recompute.  Evaluated with the row maximum taken out before the
+    exponentials (exact in real arithmetic).
+
+    q: [n_q][H_q][d]; k: [H_kv][capacity][d].  Returns [n_q][H_q].
+    """
+    q, k = _f64(q), _f64(k)
+    n_q, hq, d = q.shape
+    hkv = k.shape[0]
+    if hq % hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    if not (1 <= n_q <= length <= k.shape[1]):
+        raise ValueError("need 1 <= n_q <= length <= capacity")
+    g_size = hq // hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = np.empty((n_q, hq))
+    for i in range(n_q):
+        pos = length - n_q + i
+        for h in range(hq):
+            s = scale * (k[h // g_size, : pos + 1] @ q[i, h])
+            mx = s.max()
+            out[i, h] = mx + math.log(np.exp(s - mx).sum())
+    return out
+
+
 def sparse_key_set(length, vis_start, vis_len, idx_g):
     """Positions seen by the sparse model M_s for one KV head.
 

@@ -152,3 +152,69 @@ def test_scale_default_is_inverse_sqrt_d():
     assert np.array_equal(a, b)
     c = oracle.dense_verify(q, k, v, 10, scale=1.0)
     assert not np.allclose(a, c)
+
+
+# ------------------------------------------------------------------ row LSE
+def test_row_lse_single_key_is_the_logit():
+    """One visible key: the normaliser is that key's scaled logit exactly."""
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((1, 3, 16))
+    k = rng.standard_normal((1, 4, 16))
+    lse = oracle.row_lse(q, k, 1, scale=0.3)
+    assert np.allclose(lse[0], 0.3 * (q[0] @ k[0, 0]), rtol=0, atol=1e-15)
+
+
+def test_row_lse_equal_logits_is_log_count():
+    """q = 0 makes every logit 0, so row i (position p) has lse = log(p + 1)."""
+    q = np.zeros((5, 4, 8))
+    k = np.random.default_rng(42).standard_normal((2, 30, 8))
+    lse = oracle.row_lse(q, k, 23)
+    pos = 23 - 5 + np.arange(5)
+    assert np.allclose(lse, np.log(pos + 1.0)[:, None], rtol=0, atol=1e-14)
+
+
+def test_row_lse_shift_by_a_direction_of_q():
+    """Adding t * u to every key, with u a unit vector along q, shifts every
+    logit by scale * t * |q| and so the normaliser by the same amount."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((1, 1, 32))
+    k = rng.standard_normal((1, 50, 32))
+    u = q[0, 0] / np.linalg.norm(q[0, 0])
+    t, scale = 2.5, 0.2
+    base = oracle.row_lse(q, k, 50, scale=scale)
+    moved = oracle.row_lse(q, k + t * u, 50, scale=scale)
+    assert abs(moved[0, 0] - base[0, 0] - scale * t * np.linalg.norm(q[0, 0])) < 1e-12
+
+
+def test_row_lse_normalises_the_dense_rows():
+    """exp(s - lse) over each row's visible keys sums to 1, and weighting the
+    values with it reproduces dense_verify: the normaliser is the softmax
+    denominator of the same rows (GQA, several queries, causal rows)."""
+    rng = np.random.default_rng(44)
+    hq, hkv, d, n_q, length = 6, 2, 16, 4, 37
+    q = rng.standard_normal((n_q, hq, d)) * 1.3
+    k = rng.standard_normal((hkv, 40, d))
+    v = rng.standard_normal((hkv, 40, d))
+    lse = oracle.row_lse(q, k, length)
+    out = oracle.dense_verify(q, k, v, length)
+    for i in range(n_q):
+        pos = length - n_q + i
+        for h in range(hq):
+            g = h // (hq // hkv)
+            w = np.exp(k[g, : pos + 1] @ q[i, h] / np.sqrt(d) - lse[i, h])
+            assert abs(w.sum() - 1.0) < 1e-12
+            assert np.max(np.abs(w @ v[g, : pos + 1] - out[i, h])) < 1e-12
+
+
+def test_row_lse_matches_scipy_logsumexp():
+    """An independent library routine on the masked logits."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(45)
+    hq, hkv, d, n_q, length = 4, 1, 8, 3, 20
+    q = rng.standard_normal((n_q, hq, d)) * 2.0
+    k = rng.standard_normal((hkv, 25, d))
+    lse = oracle.row_lse(q, k, length, scale=0.7)
+    for i in range(n_q):
+        pos = length - n_q + i
+        for h in range(hq):
+            assert abs(lse[i, h] - logsumexp(0.7 * (k[0, : pos + 1] @ q[i, h]))) < 1e-12
