@@ -260,6 +260,40 @@ std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
                         int32_t* seq_len_inout_or_null, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Prefill attention of the text rows, returning their normalisers.
+ *
+ * The selection (a) starts from each text row's causal softmax normaliser
+ * (Technical summary, Methodology item 4: the top-K come from the average
+ * attention of the text tokens to the visual tokens, taken at prefill).
+ * The prefill computes those rows' attention anyway, so this call does it
+ * and returns the normaliser beside the output; passed as lse_or_null to
+ * std_select_topk, it spares the selection its first pass.
+ *
+ * Text row i (position text_start + i) of query head h (KV head
+ * h / (n_q_heads / n_kv_heads)) attends with softmax over keys
+ * [0, text_start + i]:
+ *   out[h][i]  = sum_j softmax_j(scale * q_text[h][i] . k[g][j]) v[g][j]
+ *   lse[h][i]  = log sum_j exp(scale * q_text[h][i] . k[g][j])   (natural log)
+ *
+ * q_text      [n_q_heads][n_text][head_dim] bf16 device, 16-byte aligned.
+ * kv          bf16 cache (fp32: STD_ERR_UNSUPPORTED);
+ *             text_start + n_text <= kv->len.
+ * out         [n_q_heads][n_text][head_dim] bf16 device (q_text's layout).
+ * lse_out_or_null  [n_q_heads][n_text] fp32 device, or NULL.
+ * workspace   std_prefill_text_attn_workspace() bytes (per-chunk partials:
+ *             about n_q_heads * n_text * (4 * head_dim + 12) bytes per
+ *             16,384 keys).
+ * Errors: STD_ERR_INVALID_ARGUMENT before any launch for null pointers,
+ * misalignment, text_start < 0, n_text < 1 or rows past kv->len.
+ * ------------------------------------------------------------------------ */
+size_t std_prefill_text_attn_workspace(const std_attn_shape_t* shape, int32_t text_start,
+                                       int32_t n_text);
+std_status_t std_prefill_text_attn(const std_attn_shape_t* shape, const void* q_text,
+                                   int32_t text_start, int32_t n_text, const std_kv_t* kv,
+                                   void* out, float* lse_out_or_null, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Index-list check (debug aid for (b)).
  *
  * The sparse draft calls take, per KV head, selected visual positions

@@ -9,6 +9,10 @@ binding over it (torch supplies device memory and the HIP stream):
   std_dense_verify_attn   dense verify attention (gamma+1 queries, full KV)
   std_accept              greedy longest-prefix acceptance + bonus token
 
+std_prefill_text_attn computes the prefill attention of the text rows and
+returns their softmax normalisers, which std_select_topk accepts in place of
+its own first pass.
+
 std_sparse_decode_attn_dlen / std_dense_verify_attn_dlen read the valid
 cache length from device memory, so a whole draft-verify cycle can be
 captured once and replayed; std_sparse_decode_attn_batch runs the draft
@@ -29,6 +33,7 @@ from ._lib import (  # noqa: F401
     std_sparse_decode_attn_batch, std_sparse_decode_batch_workspace,
     std_dense_verify_attn, std_dense_verify_workspace, std_dense_verify_attn_dlen,
     std_accept, std_check_idx, std_hbm_read_probe,
+    std_prefill_text_attn, std_prefill_text_attn_workspace,
     PreparedCall, prepare_dense_verify, prepare_sparse_decode, prepare_select_topk,
     prepare_accept, prepare_dense_verify_dlen, prepare_sparse_decode_dlen,
 )

@@ -76,6 +76,9 @@ _SIGS = {
     "std_accept": (ctypes.c_int, [_P, _I, _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]),
     "std_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "std_check_idx": (ctypes.c_int, [_P, _I, _I, Vis, _P, _P]),
+    "std_prefill_text_attn_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, _I]),
+    "std_prefill_text_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
+                                             ctypes.POINTER(KV), _P, _P, _P, _SZ, _P]),
 }
 
 PROBE_SINK_WORDS = 65536
@@ -371,6 +374,43 @@ def std_accept(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len
                           _stream(stream)),
            "std_accept")
     return out_tokens, n_out
+
+
+def std_prefill_text_attn_workspace(shape, text_start, n_text):
+    return load().std_prefill_text_attn_workspace(ctypes.byref(shape), int(text_start),
+                                                  int(n_text))
+
+
+def std_prefill_text_attn(q_text, k, v, length, text_start, out=None, lse_out=None,
+                          want_lse=True, scale=None, workspace=None, stream=None):
+    """Prefill attention of the text rows: q_text [H_q][n_text][d] bf16 (text
+    row i at position text_start + i) over the causal keys of the cache
+    k, v [H_kv][capacity][d] (valid length ``length``).  Returns
+    (out [H_q][n_text][d] bf16, lse [H_q][n_text] fp32 natural log or None)."""
+    lib = load()
+    for t, n in ((q_text, "q_text"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q_text.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q_text [H_q][n_text][d]; k, v [H_kv][capacity][d]")
+    hq, n_text, d = q_text.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, length)
+    if out is None:
+        out = torch.empty_like(q_text)
+    _dev(out, "out")
+    if lse_out is None and want_lse:
+        lse_out = torch.empty(hq, n_text, dtype=torch.float32, device=q_text.device)
+    if lse_out is not None:
+        _dev(lse_out, "lse_out")
+        if lse_out.dtype != torch.float32 or lse_out.numel() != hq * n_text:
+            raise ValueError("lse_out must be [H_q][n_text] float32")
+    ws = _workspace(lib.std_prefill_text_attn_workspace(ctypes.byref(shape), text_start, n_text),
+                    q_text.device, workspace)
+    _check(lib.std_prefill_text_attn(ctypes.byref(shape), _ptr(q_text), int(text_start),
+                                     int(n_text), ctypes.byref(kv), _ptr(out), _ptr(lse_out),
+                                     _ptr(ws), ws.numel(), _stream(stream)),
+           "std_prefill_text_attn")
+    return out, lse_out
 
 
 def std_check_idx(idx, vis_start, vis_len, bad_out=None, stream=None):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstdspec.so")
-SOURCES = ["api.hip", "attention.hip", "select.hip", "accept.hip", "probe.hip", "check.hip"]
+SOURCES = ["api.hip", "attention.hip", "select.hip", "accept.hip", "probe.hip", "check.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

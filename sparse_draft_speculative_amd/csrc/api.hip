@@ -9,6 +9,7 @@
 
 #include "../../include/stdspec.h"
 #include "internal.hpp"
+#include "prefill.hpp"
 
 using namespace stdspec;
 
@@ -359,6 +360,42 @@ std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
   return hip_status(launch_accept(draft, gamma, logits, vocab, logits_dtype == STD_DTYPE_BF16,
                                   out_tokens, n_out, margins_or_null, seq_len_inout_or_null,
                                   static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------ prefill text attention
+
+size_t std_prefill_text_attn_workspace(const std_attn_shape_t* s, int32_t text_start,
+                                       int32_t n_text) {
+  if (check_shape(s) != STD_OK || text_start < 0 || n_text < 1) return 0;
+  return prefill_workspace_bytes(s->n_q_heads, s->head_dim, text_start, n_text);
+}
+
+std_status_t std_prefill_text_attn(const std_attn_shape_t* s, const void* q_text,
+                                   int32_t text_start, int32_t n_text, const std_kv_t* kv,
+                                   void* out, float* lse_out_or_null, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  TRY(check_shape(s));
+  TRY(check_kv(kv, true));
+  TRY(check_extent(s, kv));
+  CHECK(kv->dtype == STD_DTYPE_BF16, STD_ERR_UNSUPPORTED,
+        "the prefill text attention takes a bf16 cache");
+  CHECK(text_start >= 0 && n_text >= 1, STD_ERR_INVALID_ARGUMENT,
+        "need text_start (%d) >= 0 and n_text (%d) >= 1", text_start, n_text);
+  CHECK((long long)text_start + n_text <= kv->len, STD_ERR_INVALID_ARGUMENT,
+        "text rows end at %lld, past len %d", (long long)text_start + n_text, kv->len);
+  CHECK((long long)s->n_q_heads * n_text <= (1LL << 30), STD_ERR_INVALID_ARGUMENT,
+        "too many text rows");
+  CHECK(q_text && out, STD_ERR_INVALID_ARGUMENT, "q_text / out is null");
+  CHECK(aligned16(q_text) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out) &&
+            ((uintptr_t)lse_out_or_null & 3) == 0,
+        STD_ERR_INVALID_ARGUMENT, "q_text, k, v, out must be 16-byte aligned, lse 4-byte");
+  TRY(check_ws(ws, ws_bytes,
+               prefill_workspace_bytes(s->n_q_heads, s->head_dim, text_start, n_text)));
+  PrefillArgs a{};
+  a.q_text = q_text; a.k = kv->k; a.v = kv->v; a.out = out; a.lse_out = lse_out_or_null;
+  a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.capacity = kv->capacity;
+  a.text_start = text_start; a.n_text = n_text; a.scale = s->scale; a.ws = ws;
+  return hip_status(launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------ index check

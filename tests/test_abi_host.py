@@ -190,6 +190,30 @@ def test_accept_rejects():
     assert lib.std_accept(p, 3, p, 10, 5, p, p, None, None, None) == E
 
 
+def test_prefill_text_attn_rejects():
+    lib = _lib.load()
+    E, U = _lib.STD_ERR_INVALID_ARGUMENT, _lib.STD_ERR_UNSUPPORTED
+    sh = _shape()
+    p = ctypes.c_void_p(FAKE)
+
+    def call(q=p, text_start=100, n_text=10, kv=None, out=p, lse=None):
+        kv = kv if kv is not None else _kv(length=200)
+        return lib.std_prefill_text_attn(ctypes.byref(sh), q, text_start, n_text,
+                                         ctypes.byref(kv), out, lse, None, 0, None)
+    assert call(q=None) == E
+    assert call(out=None) == E
+    assert call(text_start=-1) == E
+    assert call(n_text=0) == E
+    assert call(text_start=195, n_text=10) == E           # rows past len
+    assert call(q=ctypes.c_void_p(FAKE + 8)) == E          # misaligned
+    assert call(lse=ctypes.c_void_p(FAKE + 2)) == E
+    assert call(kv=_kv(length=200, dtype=_lib.STD_DTYPE_F32)) == U
+    # every argument valid: stops at the empty workspace, launches nothing
+    assert call() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert lib.std_prefill_text_attn_workspace(ctypes.byref(sh), 100, 10) > 0
+    assert lib.std_prefill_text_attn_workspace(ctypes.byref(sh), 100, 0) == 0
+
+
 def test_check_idx_rejects():
     lib = _lib.load()
     E = _lib.STD_ERR_INVALID_ARGUMENT
