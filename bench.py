@@ -61,6 +61,8 @@ def parse():
                     help="launch the calls one by one instead of replaying captured phases")
     ap.add_argument("--sel-streams", type=int, default=2,
                     help="streams the per-layer selections are dealt over")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill text attention + selection measurement")
     ap.add_argument("--no-batch", action="store_true",
                     help="skip the batched sparse draft measurement")
     ap.add_argument("--no-prefill-lse", action="store_true",
@@ -80,6 +82,14 @@ def attn_bytes_sparse(cfg, length):
     keys = cfg.topk + length - cfg.vis_len
     return (2 * cfg.n_kv_heads * keys * cfg.head_dim * e + 4 * cfg.n_kv_heads * cfg.topk
             + 2 * cfg.n_q_heads * cfg.head_dim * e)
+
+
+def prefill_flops(cfg):
+    """Matrix-unit flops of the text rows' prefill attention per layer: QK^T
+    and PV, 2 d flops per (row, visible key) each."""
+    nt = cfg.n_text
+    pairs = nt * cfg.text_start + nt * (nt + 1) // 2
+    return 4 * cfg.head_dim * cfg.n_q_heads * pairs
 
 
 def select_flops(cfg):
@@ -320,6 +330,55 @@ def main():
                        "note": "step 1 (row LSE) supplied by the caller, as the prefill's "
                                "attention returns it; steps 2-3 timed"}
 
+    # Selection beside the prefill: the text rows' prefill attention returns
+    # their normalisers (std_prefill_text_attn) and the selection takes
+    # those instead of computing its first pass
+    pf = None
+    if not args.no_prefill:
+        pf_ws = torch.zeros(max(sd.std_prefill_text_attn_workspace(shape, cfg.text_start,
+                                                                   cfg.n_text), 256),
+                            dtype=torch.uint8, device=dev)
+        pf_out = torch.empty_like(layers[0]["q_text"])
+        pf_lse = [torch.empty(cfg.n_q_heads, cfg.n_text, dtype=torch.float32, device=dev)
+                  for _ in range(L)]
+        pf_calls = [sd.prepare_prefill_text_attn(lay["q_text"], lay["k"], lay["v"], cfg.ctx,
+                                                 cfg.text_start, pf_out, pf_lse[l], pf_ws,
+                                                 stream=st)
+                    for l, lay in enumerate(layers)]
+        idx3 = [torch.zeros_like(t) for t in idx]
+        sel3 = [sd.prepare_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
+                                       cfg.vis_start, cfg.vis_len, cfg.topk, idx3[l],
+                                       ws_sels[l % nss], lse=pf_lse[l], stream=st_sel[l % nss])
+                for l, lay in enumerate(layers)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            for c in pf_calls:                 # warm-up
+                c()
+            select_all(sel3)
+        torch.cuda.synchronize()
+        e0, e1, e2 = ev(), ev(), ev()
+        with torch.cuda.stream(st):
+            e0.record()
+            for c in pf_calls:
+                c()
+            e1.record()
+            select_all(sel3)
+            e2.record()
+        torch.cuda.synchronize()
+        pf_ms, sel3_ms = e0.elapsed_time(e1) / L, e1.elapsed_time(e2) / L
+        same = sum(len(set(a.tolist()) & set(b.tolist()))
+                   for x, y in zip(idx, idx3) for a, b in zip(x.cpu(), y.cpu()))
+        pf_flops = prefill_flops(cfg)
+        pf = {"prefill_ms_per_layer": round(pf_ms, 3),
+              "prefill_tflops": round(pf_flops / (pf_ms * 1e-3) / 1e12, 1),
+              "prefill_frac_of_bf16_peak": round(pf_flops / (pf_ms * 1e-3) / PEAK_BF16, 4),
+              "selection_ms_per_layer": round(sel3_ms, 3),
+              "idx_overlap_with_full_selection": round(same / (L * cfg.n_kv_heads * cfg.topk),
+                                                       6),
+              "note": "std_prefill_text_attn (output + normalisers of the 2,048 text rows over "
+                      "their causal keys, 28 layers), then the 28 selections fed those "
+                      "normalisers"}
+
     batch_sparse = None if args.no_batch else batched_sparse(sd, cfg, layers[0], idx[0], st)
 
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
@@ -402,6 +461,7 @@ def main():
         "dense_only_attn_gbps": round(dense_gbps, 1),
         "cycle_ms": cycle_stats(cycle_ms),
         "selection_prefill_lse": sel_prefill,
+        "prefill_then_selection": pf,
         "batched_sparse": batch_sparse,
         "hbm_read_probe": probe,
         "projection": projection(cycle_ms, G, dense_ms_per_tok),

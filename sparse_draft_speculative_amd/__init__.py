@@ -36,4 +36,5 @@ from ._lib import (  # noqa: F401
     std_prefill_text_attn, std_prefill_text_attn_workspace,
     PreparedCall, prepare_dense_verify, prepare_sparse_decode, prepare_select_topk,
     prepare_accept, prepare_dense_verify_dlen, prepare_sparse_decode_dlen,
+    prepare_prefill_text_attn,
 )

@@ -525,6 +525,20 @@ def prepare_sparse_decode_dlen(q, k, v, vis_start, vis_len, idx, out, workspace,
                         (shape, kv, q, k, v, idx, out, workspace, len_dev))
 
 
+def prepare_prefill_text_attn(q_text, k, v, length, text_start, out, lse_out, workspace,
+                              stream=None, scale=None):
+    for t, n in ((q_text, "q_text"), (k, "k"), (v, "v"), (out, "out"), (lse_out, "lse_out"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    hq, n_text, d = q_text.shape
+    shape = attn_shape(hq, k.shape[0], d, scale)
+    kv = kv_desc(k, v, length)
+    args = (ctypes.byref(shape), _ptr(q_text), int(text_start), n_text, ctypes.byref(kv),
+            _ptr(out), _ptr(lse_out), _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall("std_prefill_text_attn", args, kv,
+                        (shape, kv, q_text, k, v, out, lse_out, workspace))
+
+
 def prepare_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, idx_out,
                         workspace, scores_out=None, lse=None, stream=None, scale=None):
     for t, n in ((q_text, "q_text"), (k, "k"), (idx_out, "idx_out"), (workspace, "workspace")):

@@ -8,16 +8,15 @@
 // row i, and lse = log of that softmax's denominator, which the selection
 // call accepts in place of computing it.
 //
-//  prefill_mfma_kernel -- one workgroup = 8 waves x 2 row blocks x 16 rows =
-//      256 rows of one KV head group (the G heads' rows stacked, as the
-//      selection kernels lay them out) against one chunk of kPfChunk keys.
-//      Q stays in registers; K and V tiles of 64 keys move global -> LDS by
-//      direct-to-LDS copies (four buffers, three tiles in flight).  Per tile
-//      and row block: S^T = K Q^T on the matrix unit, the row's running max
-//      (shared by the row's four lanes), P = 2^(s c - m), O^T += V^T P^T on
-//      the matrix unit with V^T taken by transpose reads, each fragment
-//      serving both row blocks.  The chunk's (m, l, O) per row go to the
-//      workspace.
+//  prefill_mfma_kernel -- one workgroup = 16 waves x 16 rows = 256 rows of
+//      one KV head group (the G heads' rows stacked, as the selection
+//      kernels lay them out) against one chunk of kPfChunk keys, four waves
+//      per SIMD.  Q stays in registers; K and V tiles of 64 keys move
+//      global -> LDS by direct-to-LDS copies (four buffers, three tiles in
+//      flight).  Per tile: S^T = K Q^T on the matrix unit, the row's running
+//      max (shared by the row's four lanes), P = 2^(s c - m), O^T += V^T P^T
+//      on the matrix unit with V^T taken by transpose reads.  The chunk's
+//      (m, l, O) per row go to the workspace.
 //  prefill_merge -- one wave per row: merges the chunks into O (bf16) and
 //      the natural-log normaliser.
 
@@ -29,12 +28,22 @@
 namespace stdspec {
 namespace {
 
-constexpr int kPfWaves = 8;
+constexpr int kPfWaves = 16;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfRB = 2;                                  // 16-row blocks per wave
+constexpr int kPfRB = 1;                                  // 16-row blocks per wave
 constexpr int kPfRowsWg = kPfWaves * 16 * kPfRB;          // rows per workgroup
+constexpr int kPfOcc = kPfWaves / 4;                      // waves per SIMD
 constexpr int kPfBufs = 4;                                // tile buffers (a power of two)
 constexpr int kPfXcds = 8;
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to one dword of two bf16 (round to nearest even), one
+// conversion for the pair.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t));
+}
 
 // Consecutive items (the row blocks of one KV head and key chunk) go to the
 // same XCD, so the K and V tiles they share are fetched into one L2.
@@ -44,15 +53,19 @@ __device__ __forceinline__ int pf_item(int bid, int n_items) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
+__global__ __launch_bounds__(kPfThreads, kPfOcc) void prefill_mfma_kernel(
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, int text_start, int n_text,
     float c, int n_chunks, int n_rb, float* __restrict__ m_part, double* __restrict__ l_part,
     float* __restrict__ o_part) {
   constexpr int KST = D / 32, DB = D / 16, CPR = D / 8;
   constexpr int TILE = 64 * D;
-  constexpr int LPT = 64 * CPR / kPfThreads;   // copies per thread, tensor and tile
-  static_assert(LPT * kPfThreads == 64 * CPR, "a tile is a whole number of copies per thread");
+  // 16-byte copies per tensor and tile; with fewer copies than threads the
+  // first COPIES threads (whole waves) issue one each
+  constexpr int COPIES = 64 * CPR;
+  constexpr int LPT = COPIES >= kPfThreads ? COPIES / kPfThreads : 1;
+  static_assert(COPIES % kPfThreads == 0 || kPfThreads % COPIES == 0, "copies per thread");
+  static_assert(COPIES % 64 == 0, "copying threads form whole waves");
   constexpr int NB = kPfBufs;
   __shared__ __align__(16) uint16_t smem[NB * 2 * TILE];   // [buffer][K, V]
 
@@ -92,6 +105,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   // (thread tid fills 16-byte slots kPfThreads*u + tid); rows past the
   // chunk re-read its last key.
   auto issue = [&](int tt) {
+    if (COPIES < kPfThreads && tid >= COPIES) return;          // wave-uniform
     uint16_t* kb = smem + (tt & (NB - 1)) * 2 * TILE;
     uint16_t* vb = kb + TILE;
 #pragma unroll
@@ -142,37 +156,46 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     // keys at or before text_start are visible to every text row
     const bool interior = t0 + 64 <= key1 && t0 + 63 <= text_start;
 
-    // S^T = K Q^T: lane (col, grp) gets keys t0 + kb*16 + 4 grp + i of row col
+    // S^T = K Q^T: lane (col, grp) gets keys t0 + kb*16 + 4 grp + i of row
+    // col; the K fragments of two key blocks are read before their MFMAs
     floatx4_t sacc[kPfRB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4_t a[KST];
+    for (int kp = 0; kp < 4; kp += 2) {
+      u32x4_t a[2][KST];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk)
+          a[b2][kk] = *reinterpret_cast<const u32x4_t*>(
+              Ks + Tile<D>::off_k((kp + b2) * 16 + col, KST * grp + kk));
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < kPfRB; ++r) sacc[r][kp + b2] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk)
-        a[kk] = *reinterpret_cast<const u32x4_t*>(Ks + Tile<D>::off_k(kb * 16 + col, KST * grp + kk));
 #pragma unroll
-      for (int r = 0; r < kPfRB; ++r) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int kk = 0; kk < KST; ++kk) acc = mfma_bf16(as_bf16x8(a[kk]), qb[r][kk], acc);
-        sacc[r][kb] = acc;
-      }
+          for (int r = 0; r < kPfRB; ++r)
+            sacc[r][kp + b2] = mfma_bf16(as_bf16x8(a[b2][kk]), qb[r][kk], sacc[r][kp + b2]);
     }
 
-    // scale, mask, running max per row (the row's four lanes agree), P
-    float p[kPfRB][16];
+    // mask, running max per row on the raw scores (c > 0; the row's four
+    // lanes agree), P = 2^(s c - m) with the scale folded into one FMA
+    uint32_t pw[kPfRB][8];
 #pragma unroll
     for (int r = 0; r < kPfRB; ++r) {
       float x[16];
-      float tmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float sv = sacc[r][j >> 2][j & 3] * c;
         const int key = t0 + (j >> 2) * 16 + 4 * grp + (j & 3);
-        x[j] = (interior || (key < key1 && key <= rpos[r])) ? sv : -INFINITY;
-        tmax = fmaxf(tmax, x[j]);
+        x[j] = (interior || (key < key1 && key <= rpos[r])) ? sacc[r][j >> 2][j & 3] : -INFINITY;
       }
-      tmax = max_over_groups(tmax);
+      float tmax = x[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
+      tmax = max_over_groups(tmax) * c;
       if (tmax > m[r] + 8.f) {            // rare after the first tile; also while m = -inf
         const float alpha = (m[r] == -INFINITY) ? 0.f : fast_exp2(m[r] - tmax);
         l[r] *= (double)alpha;
@@ -180,41 +203,42 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
         for (int db = 0; db < DB; ++db) oacc[r][db] *= alpha;
         m[r] = tmax;
       }
-      const float ms = (m[r] == -INFINITY) ? 0.f : m[r];
+      const float nms = (m[r] == -INFINITY) ? 0.f : -m[r];
+      float pj[16];
       float ts = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        p[r][j] = fast_exp2(x[j] - ms);
-        ts += p[r][j];
+        pj[j] = fast_exp2(fmaf(x[j], c, nms));
+        ts += pj[j];
       }
       l[r] += (double)ts;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[r][w] = pack2_bf16(pj[2 * w], pj[2 * w + 1]);
     }
 
-    // O^T += V^T P^T in two 32-key steps; the B operand holds the lane's own
-    // probabilities (keys 32 ks + 4 grp + j, then 32 ks + 16 + 4 grp + j)
-    // and the transpose reads of V follow the same key order
+    // O^T += V^T P^T in two 32-key steps.  The B operand holds the lane's
+    // own probabilities (keys 32 ks + 4 grp + j, then 32 ks + 16 + 4 grp +
+    // j) and the transpose reads of V follow the same key order; every V^T
+    // fragment of a step is read before its MFMAs, and each serves all the
+    // wave's row blocks.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t pb[kPfRB];
-#pragma unroll
-      for (int r = 0; r < kPfRB; ++r) {
-        uint4 w;
-        w.x = pack_bf16x2(p[r][8 * ks + 0], p[r][8 * ks + 1]);
-        w.y = pack_bf16x2(p[r][8 * ks + 2], p[r][8 * ks + 3]);
-        w.z = pack_bf16x2(p[r][8 * ks + 4], p[r][8 * ks + 5]);
-        w.w = pack_bf16x2(p[r][8 * ks + 6], p[r][8 * ks + 7]);
-        pb[r] = as_bf16x8(w);
-      }
       const int vrow = 32 * ks + 4 * grp + r4;
+      uint4 va[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int chunk = 2 * db + (rc >> 1);
         const int e = 4 * (rc & 1);
         const uint2 lo = lds_read_tr16(Vs + Tile<D>::off_v(vrow, chunk) + e);
         const uint2 hi = lds_read_tr16(Vs + Tile<D>::off_v(vrow + 16, chunk) + e);
-        const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        va[db] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
 #pragma unroll
-        for (int r = 0; r < kPfRB; ++r) oacc[r][db] = mfma_bf16(va, pb[r], oacc[r][db]);
+      for (int r = 0; r < kPfRB; ++r) {
+        const bf16x8_t pb = as_bf16x8(make_uint4(pw[r][4 * ks + 0], pw[r][4 * ks + 1],
+                                                 pw[r][4 * ks + 2], pw[r][4 * ks + 3]));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[r][db] = mfma_bf16(as_bf16x8(va[db]), pb, oacc[r][db]);
       }
     }
   }
