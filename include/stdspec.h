@@ -317,7 +317,8 @@ std_status_t std_check_idx(const int32_t* idx, int32_t n_kv_heads, int32_t topk,
  * (Technical summary, Methodology item 2: the sparse mode cuts draft-phase
  * I/O; the verify pass reads the full cache once).  This call reads
  * [buf, buf + bytes) once with a fixed grid of 256 workgroups x 256 lanes
- * in 16 KB tiles (tile t to workgroup t mod 256) and does nothing else, so
+ * in 16 KB tiles (tile t to workgroup t mod 256), with non-temporal 16-byte
+ * loads, and does nothing else, so
  * timing it on a buffer larger than the 256 MB last-level cache gives the
  * read bandwidth this part attains, the yardstick beside the nominal peak.
  *

@@ -179,7 +179,8 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, bool ok, in
 // s + S, s + 2S, ... (S splits, a function of len and H_kv only), so at any
 // moment the workgroups of a head sweep one contiguous region of the cache.
 // K and V tiles move global -> LDS by direct-to-LDS copies (no staging
-// registers) into three buffers, two tiles in flight.  Wave w reduces key
+// registers, non-temporal: each byte is read once per call) into three
+// buffers, two tiles in flight.  Wave w reduces key
 // half w & 1 of every tile for the 16 query rows of block w >> 1; the two
 // key halves are merged in LDS at the end.  Every K/V byte is read from HBM
 // once per call when n_q * G <= 64.
@@ -202,8 +203,8 @@ __device__ __forceinline__ void dense_issue_tile(uint16_t* ks, uint16_t* vs, con
     const int row = slot / CPR, phys = slot % CPR;
     const size_t base = (size_t)min(t0 + row, len - 1) * D;
     const uint32_t dst = (kDenseThreads * u + 64 * wave) * 16;
-    dma16(kh + base + (Tile<D>::slot_k(row, phys) << 3), lds_addr(ks) + dst);
-    dma16(vh + base + (Tile<D>::slot_v(row, phys) << 3), lds_addr(vs) + dst);
+    dma16_stream(kh + base + (Tile<D>::slot_k(row, phys) << 3), lds_addr(ks) + dst);
+    dma16_stream(vh + base + (Tile<D>::slot_v(row, phys) << 3), lds_addr(vs) + dst);
   }
 }
 

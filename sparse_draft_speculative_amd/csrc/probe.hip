@@ -5,8 +5,9 @@
 // the bandwidth a plain sweep actually attains beside the nominal 8 TB/s.
 //
 // A fixed grid of one workgroup per CU walks the buffer in 16 KB tiles,
-// tile t going to workgroup t mod grid; each lane issues four 16-byte loads
-// per tile, two tiles in flight.  The loaded words are folded into an XOR
+// tile t going to workgroup t mod grid; each lane issues four 16-byte
+// non-temporal loads per tile (the hint reads a once-read stream faster),
+// two tiles in flight.  The loaded words are folded into an XOR
 // digest (one word per lane) so the loads cannot be dropped; its value has
 // no meaning beyond that.
 
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe(const u32x4_t* _
     const u32x4_t* src = p + t * kProbeTile16 + threadIdx.x;
     u32x4_t x[kProbeLoads];
 #pragma unroll
-    for (int i = 0; i < kProbeLoads; ++i) x[i] = src[i * kProbeThreads];
+    for (int i = 0; i < kProbeLoads; ++i) x[i] = __builtin_nontemporal_load(src + i * kProbeThreads);
 #pragma unroll
     for (int i = 0; i < kProbeLoads; ++i) acc ^= x[i];
   }
