@@ -666,15 +666,19 @@ KERNEL_SOURCES = ["attention.hip", "tile.hpp", "common.hpp", "internal.hpp"]
 
 
 def kernel_source_digest():
-    """sha256 over the dense verify kernel's sources (counter values taken
-    on other sources do not describe this kernel)."""
+    """sha256 over the dense verify kernel's sources with comments and
+    whitespace removed (counter values taken on other code do not describe
+    this kernel; an edited comment does not change it)."""
     import hashlib
     h = hashlib.sha256()
     base = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "sparse_draft_speculative_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(base, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(base, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

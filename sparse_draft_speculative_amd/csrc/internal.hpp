@@ -24,9 +24,10 @@ inline int pow2_floor(long long x) {
 // order whatever the number of rows in the call.  S is sized so one layer
 // launches about 208 workgroups, one round at one per CU.  Measured on the
 // 140k-key layer: 208 workgroups with two tiles in flight each stream the
-// cache faster than 256 with three (56.8 against 59.1 us per call); past
-// about 13 MB in flight the HBM requests contend, below about 160
-// workgroups too few are in flight.
+// cache faster than 256 with three (52.9 against 54.0 us per call with
+// non-temporal copies, 56.8 against 59.1 without); past about 13 MB in
+// flight the HBM requests contend, below about 160 workgroups too few are
+// in flight.
 constexpr int kDenseWorkgroups = 208;
 inline int dense_split_count(int len, int n_kv_heads) {
   const int tiles = (len + 63) / 64;
