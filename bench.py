@@ -502,30 +502,19 @@ def read_probe(sd, nbytes, regions=4, reps=40):
 
 
 def batched_sparse(sd, cfg, lay, idx, st, batches=(1, 4, 16), reps=20):
-    """Sparse draft attention of one c4 layer for B independent sequences in
-    one launch (std_sparse_decode_attn_batch; B copies of the layer's cache
-    and index list at distinct addresses), each at length ctx + 1: HBM GB/s
-    against B x the single-sequence algorithmic bytes."""
+    """Sparse draft attention and dense verify attention of one c4 layer for
+    B independent sequences, one launch each (std_sparse_decode_attn_batch,
+    std_dense_verify_attn_batch; B copies of the layer's cache and index
+    list at distinct addresses), each sequence at ctx + 1 keys for the draft
+    step and ctx + gamma + 1 for the verify pass: HBM GB/s against B x the
+    single-sequence algorithmic bytes."""
     import torch
-    out = {"layer_bytes_per_sequence": int(attn_bytes_sparse(cfg, cfg.ctx + 1))}
-    L = cfg.ctx + 1
-    for B in batches:
-        k = lay["k"][None].expand(B, *lay["k"].shape).contiguous()
-        v = lay["v"][None].expand(B, *lay["v"].shape).contiguous()
-        q = lay["q_draft"][0][None].expand(B, *lay["q_draft"][0].shape).contiguous()
-        ib = idx[None].expand(B, *idx.shape).contiguous()
-        o = torch.empty_like(q)
-        shape = sd.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
-        ws = torch.zeros(max(sd.std_sparse_decode_batch_workspace(shape, B, k, L, cfg.vis_start,
-                                                                  cfg.vis_len, cfg.topk), 256),
-                         dtype=torch.uint8, device=q.device)
+    G = cfg.gamma
+    sp_bytes = int(attn_bytes_sparse(cfg, cfg.ctx + 1))
+    dv_bytes = int(attn_bytes_dense(cfg, cfg.verify_len, G + 1))
+    out = {"layer_bytes_per_sequence": sp_bytes, "verify_bytes_per_sequence": dv_bytes}
 
-        # the copies above ran on the current stream, the calls run on st
-        torch.cuda.synchronize()
-
-        def call():
-            sd.std_sparse_decode_attn_batch(q, k, v, L, cfg.vis_start, cfg.vis_len, ib, out=o,
-                                            workspace=ws, stream=st)
+    def timed(call):
         for _ in range(3):
             call()
         torch.cuda.synchronize()
@@ -536,11 +525,38 @@ def batched_sparse(sd, cfg, lay, idx, st, batches=(1, 4, 16), reps=20):
                 call()
             e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        gbps = B * out["layer_bytes_per_sequence"] / (us * 1e-6) / 1e9
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    for B in batches:
+        k = lay["k"][None].expand(B, *lay["k"].shape).contiguous()
+        v = lay["v"][None].expand(B, *lay["v"].shape).contiguous()
+        q = lay["q_draft"][0][None].expand(B, *lay["q_draft"][0].shape).contiguous()
+        qv = lay["q_verify"][None].expand(B, *lay["q_verify"].shape).contiguous()
+        ib = idx[None].expand(B, *idx.shape).contiguous()
+        o = torch.empty_like(q)
+        ov = torch.empty_like(qv)
+        shape = sd.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+        ws = torch.zeros(max(sd.std_sparse_decode_batch_workspace(shape, B, k, cfg.ctx + 1,
+                                                                  cfg.vis_start, cfg.vis_len,
+                                                                  cfg.topk), 256),
+                         dtype=torch.uint8, device=q.device)
+        wsv = torch.zeros(max(sd.std_dense_verify_batch_workspace(shape, G + 1, B, k,
+                                                                  cfg.verify_len), 256),
+                          dtype=torch.uint8, device=q.device)
+        # the copies above ran on the current stream, the calls run on st
+        torch.cuda.synchronize()
+        us = timed(lambda: sd.std_sparse_decode_attn_batch(
+            q, k, v, cfg.ctx + 1, cfg.vis_start, cfg.vis_len, ib, out=o, workspace=ws, stream=st))
+        usv = timed(lambda: sd.std_dense_verify_attn_batch(
+            qv, k, v, cfg.verify_len, out=ov, workspace=wsv, stream=st))
+        gbps = B * sp_bytes / (us * 1e-6) / 1e9
+        gbpsv = B * dv_bytes / (usv * 1e-6) / 1e9
         out[f"batch{B}"] = {"us_per_launch": round(us, 2), "achieved_gbps": round(gbps, 1),
-                            "frac": round(gbps * 1e9 / PEAK_HBM, 4)}
-        del k, v, q, ib, o, ws
+                            "frac": round(gbps * 1e9 / PEAK_HBM, 4),
+                            "verify_us_per_launch": round(usv, 2),
+                            "verify_gbps": round(gbpsv, 1),
+                            "verify_frac": round(gbpsv * 1e9 / PEAK_HBM, 4)}
+        del k, v, q, qv, ib, o, ov, ws, wsv
         torch.cuda.empty_cache()
     return out
 

@@ -234,6 +234,29 @@ std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* shape, const v
                                           void* stream);
 
 /* ------------------------------------------------------------------------
+ * (c, batched) Dense verify attention for `batch` independent sequences in
+ * one launch, each as std_dense_verify_attn (Technical summary, Methodology
+ * items 2-3: one pass of the dense model over each sequence's full cache
+ * verifies its gamma drafts).
+ *
+ * q    [batch][n_q][n_q_heads][head_dim]; out the same layout.
+ * kv   kv->k, kv->v point at [batch][n_kv_heads][capacity][head_dim];
+ *      kv->len is the bound every sequence's length is clamped to.
+ * len_dev  NULL (every sequence has length kv->len) or [batch] int32
+ *      device: sequence b uses min(max(len_dev[b] + len_offset, 1), kv->len).
+ * bf16 only for batch > 1 (fp32: STD_ERR_UNSUPPORTED); batch = 1 is
+ * std_dense_verify_attn(_dlen) bit for bit.  With batch > 1 the key split
+ * count is raised so the grid fills whole rounds of the machine, which can
+ * change the summation order (results stay within the same tolerance).
+ * ------------------------------------------------------------------------ */
+size_t std_dense_verify_batch_workspace(const std_attn_shape_t* shape, int32_t n_q,
+                                        int32_t batch, const std_kv_t* kv);
+std_status_t std_dense_verify_attn_batch(const std_attn_shape_t* shape, const void* q,
+                                         int32_t n_q, int32_t batch, const std_kv_t* kv,
+                                         const int32_t* len_dev, int32_t len_offset, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * (d) Greedy acceptance plus the bonus token.
  *
  * Technical summary, Methodology item 3: verification finds the longest
@@ -258,6 +281,16 @@ std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
                         int32_t vocab, std_dtype_t logits_dtype, int32_t* out_tokens,
                         int32_t* n_out, float* margins_or_null,
                         int32_t* seq_len_inout_or_null, void* stream);
+
+/* (d, batched) Acceptance for `batch` sequences with the same gamma, each as
+ * std_accept: draft [batch][gamma], logits [batch][gamma+1][vocab],
+ * out_tokens [batch][gamma+1], n_out [batch], margins [batch][gamma+1] or
+ * NULL, seq_len [batch] or NULL (sequence b's length advances by its own
+ * n + 1).  batch = 1 is std_accept. */
+std_status_t std_accept_batch(const int32_t* draft, int32_t gamma, int32_t batch,
+                              const void* logits, int32_t vocab, std_dtype_t logits_dtype,
+                              int32_t* out_tokens, int32_t* n_out, float* margins_or_null,
+                              int32_t* seq_len_inout_or_null, void* stream);
 
 /* ------------------------------------------------------------------------
  * Prefill attention of the text rows, returning their normalisers.

@@ -75,6 +75,11 @@ _SIGS = {
                                        ctypes.POINTER(KV), Vis, _I, _P, _P, _P, _P, _SZ, _P]),
     "std_accept": (ctypes.c_int, [_P, _I, _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]),
     "std_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "std_dense_verify_batch_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, _I,
+                                               ctypes.POINTER(KV)]),
+    "std_dense_verify_attn_batch": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
+                                                   ctypes.POINTER(KV), _P, _I, _P, _P, _SZ, _P]),
+    "std_accept_batch": (ctypes.c_int, [_P, _I, _I, _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]),
     "std_check_idx": (ctypes.c_int, [_P, _I, _I, Vis, _P, _P]),
     "std_prefill_text_attn_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, _I]),
     "std_prefill_text_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
@@ -179,6 +184,43 @@ def std_dense_verify_attn(q, k, v, length, out=None, scale=None, workspace=None,
     _check(lib.std_dense_verify_attn(ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv),
                                      _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "std_dense_verify_attn")
+    return out
+
+
+def std_dense_verify_batch_workspace(shape, n_q, batch, k, length):
+    """Workspace bytes of std_dense_verify_attn_batch; k [B][H_kv][capacity][d]."""
+    kv = KV(k.data_ptr(), 0, k.shape[2], int(length), _dtype_code(k))
+    return load().std_dense_verify_batch_workspace(ctypes.byref(shape), int(n_q), int(batch),
+                                                   ctypes.byref(kv))
+
+
+def std_dense_verify_attn_batch(q, k, v, max_len, len_dev=None, len_offset=0, out=None,
+                                scale=None, workspace=None, stream=None):
+    """Dense verify for B sequences in one launch.  q [B][n_q][H_q][d];
+    k, v [B][H_kv][capacity][d]; len_dev None (every sequence has length
+    max_len) or [B] int32 device lengths: min(max(len_dev[b] + len_offset, 1),
+    max_len)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    B, n_q, hq, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or v.shape != k.shape:
+        raise ValueError("k and v must be [B][H_kv][capacity][d] with the batch of q")
+    if len_dev is not None:
+        _dev(len_dev, "len_dev")
+        if len_dev.dtype != torch.int32 or len_dev.numel() != B:
+            raise ValueError("len_dev must be [B] int32")
+    shape = attn_shape(hq, k.shape[1], d, scale)
+    kv = KV(k.data_ptr(), v.data_ptr(), k.shape[2], int(max_len), _dtype_code(k))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    ws = _workspace(std_dense_verify_batch_workspace(shape, n_q, B, k, max_len), q.device,
+                    workspace)
+    _check(lib.std_dense_verify_attn_batch(ctypes.byref(shape), _ptr(q), n_q, B, ctypes.byref(kv),
+                                           _ptr(len_dev), int(len_offset), _ptr(out), _ptr(ws),
+                                           ws.numel(), _stream(stream)),
+           "std_dense_verify_attn_batch")
     return out
 
 
@@ -445,6 +487,29 @@ def std_hbm_read_probe(buf, sink=None, stream=None):
                                   _stream(stream)),
            "std_hbm_read_probe")
     return sink
+
+
+def std_accept_batch(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len=None,
+                     stream=None):
+    """Greedy acceptance for B sequences.  draft [B][gamma] int32; logits
+    [B][gamma+1][vocab].  Returns (out_tokens [B][gamma+1], n_out [B])."""
+    lib = load()
+    _dev(draft, "draft")
+    _dev(logits, "logits")
+    B, gamma = draft.shape
+    vocab = logits.shape[2]
+    if logits.shape[:2] != (B, gamma + 1):
+        raise ValueError("logits must be [B][gamma+1][vocab]")
+    dev = logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty(B, gamma + 1, dtype=torch.int32, device=dev)
+    if n_out is None:
+        n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib.std_accept_batch(_ptr(draft), gamma, B, _ptr(logits), vocab, _dtype_code(logits),
+                                _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len),
+                                _stream(stream)),
+           "std_accept_batch")
+    return out_tokens, n_out
 
 
 # ----------------------------------------------------------------------------

@@ -92,6 +92,12 @@ __global__ __launch_bounds__(64) void accept_commit(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ out_tokens,
                                                     int32_t* __restrict__ n_out,
                                                     int32_t* __restrict__ seq_len) {
+  // workgroup b: sequence b of a batch ([b][gamma] drafts, [b][gamma+1] tokens)
+  const int b = blockIdx.x;
+  draft += (size_t)b * gamma;
+  out_tokens += (size_t)b * (gamma + 1);
+  n_out += b;
+  if (seq_len) seq_len += b;
   __shared__ int sh_n;
   const int lane = threadIdx.x;
   if (lane == 0) sh_n = gamma;
@@ -117,18 +123,21 @@ __global__ __launch_bounds__(64) void accept_commit(const int32_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_accept(const int32_t* draft, int gamma, const void* logits, int vocab, bool bf16,
-                         int32_t* out_tokens, int32_t* n_out, float* margins, int32_t* seq_len,
-                         hipStream_t st) {
+hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const void* logits,
+                         int vocab, bool bf16, int32_t* out_tokens, int32_t* n_out, float* margins,
+                         int32_t* seq_len, hipStream_t st) {
+  // one argmax workgroup per logit row of every sequence ([batch][gamma+1]
+  // rows back to back), then one commit wave per sequence
+  const int rows = batch * (gamma + 1);
   if (bf16)
-    argmax_rows<uint16_t><<<gamma + 1, kArgmaxThreads, 0, st>>>(static_cast<const uint16_t*>(logits), vocab,
-                                                     out_tokens, margins);
+    argmax_rows<uint16_t><<<rows, kArgmaxThreads, 0, st>>>(
+        static_cast<const uint16_t*>(logits), vocab, out_tokens, margins);
   else
-    argmax_rows<float><<<gamma + 1, kArgmaxThreads, 0, st>>>(static_cast<const float*>(logits), vocab,
-                                                  out_tokens, margins);
+    argmax_rows<float><<<rows, kArgmaxThreads, 0, st>>>(static_cast<const float*>(logits), vocab,
+                                                       out_tokens, margins);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  accept_commit<<<1, 64, 0, st>>>(draft, gamma, out_tokens, n_out, seq_len);
+  accept_commit<<<batch, 64, 0, st>>>(draft, gamma, out_tokens, n_out, seq_len);
   return hipGetLastError();
 }
 

@@ -99,9 +99,19 @@ int sparse_splits(const std_kv_t* kv, std_vis_t vis, int topk) {
   return (L + kSparseChunk - 1) / kSparseChunk;
 }
 
-int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int* chunk) {
+// One sequence: dense_split_count.  A batch of several runs in rounds of
+// 256 workgroups (one per CU), so its split count is raised until the grid
+// fills whole rounds (the row blocks of a sequence count once here: at the
+// verify shapes a sequence has one).
+int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int* chunk, int batch = 1) {
   *chunk = 64;                                   // tile size; splits interleave tiles
-  return dense_split_count(kv->len, s->n_kv_heads);
+  const int S = dense_split_count(kv->len, s->n_kv_heads);
+  if (batch <= 1) return S;
+  const long long per_round = 256, wg = (long long)batch * s->n_kv_heads;
+  const long long rounds = (wg * S + per_round - 1) / per_round;
+  const long long full = (rounds * per_round) / wg;
+  const int tiles = (kv->len + 63) / 64;
+  return (int)(full < tiles ? (full > S ? full : S) : tiles);
 }
 
 std_status_t check_ws(void* ws, size_t have, size_t need) {
@@ -154,7 +164,7 @@ size_t std_dense_verify_workspace(const std_attn_shape_t* s, int32_t n_q, const 
 
 namespace {
 
-std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q,
+std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q, int32_t batch,
                           const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
                           void* out, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_shape(s));
@@ -163,18 +173,25 @@ std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q,
   CHECK(q && out, STD_ERR_INVALID_ARGUMENT, "q / out is null");
   CHECK(n_q >= 1 && n_q <= kv->len, STD_ERR_INVALID_ARGUMENT, "need 1 <= n_q (%d) <= len (%d)",
         n_q, kv->len);
-  CHECK((long long)n_q * s->n_q_heads <= (1 << 24), STD_ERR_INVALID_ARGUMENT,
-        "too many query rows");
+  CHECK(batch >= 1 && (long long)batch * n_q * s->n_q_heads <= (1 << 24),
+        STD_ERR_INVALID_ARGUMENT, "need batch (%d) >= 1 and batch * n_q * n_q_heads <= 2^24",
+        batch);
   CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
         STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
+  if (batch > 1) {
+    const long long n_rb = ((long long)n_q * (s->n_q_heads / s->n_kv_heads) + 63) / 64;
+    CHECK(kv->dtype == STD_DTYPE_BF16, STD_ERR_UNSUPPORTED, "batched dense verify needs bf16 KV");
+    CHECK(batch * n_rb <= 65535, STD_ERR_INVALID_ARGUMENT,
+          "batch * row blocks (%lld) exceeds the grid", batch * n_rb);
+  }
   int chunk;
-  const int splits = dense_splits(s, kv, &chunk);
-  const SplitWorkspace w = split_workspace(splits, n_q * s->n_q_heads, s->head_dim);
+  const int splits = dense_splits(s, kv, &chunk, batch);
+  const SplitWorkspace w = split_workspace(splits, batch * n_q * s->n_q_heads, s->head_dim);
   TRY(check_ws(ws, ws_bytes, w.bytes()));
   AttnArgs a{};
   a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
-  a.capacity = kv->capacity; a.len = kv->len; a.n_q = n_q;
+  a.capacity = kv->capacity; a.len = kv->len; a.n_q = n_q; a.batch = batch;
   a.len_dev = len_dev; a.len_off = len_off;
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = false;
@@ -191,7 +208,7 @@ extern "C" {
 std_status_t std_dense_verify_attn(const std_attn_shape_t* s, const void* q, int32_t n_q,
                                    const std_kv_t* kv, void* out, void* ws, size_t ws_bytes,
                                    void* stream) {
-  return dense_verify(s, q, n_q, kv, nullptr, 0, out, ws, ws_bytes, stream);
+  return dense_verify(s, q, n_q, 1, kv, nullptr, 0, out, ws, ws_bytes, stream);
 }
 
 std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* s, const void* q, int32_t n_q,
@@ -199,7 +216,24 @@ std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* s, const void* q
                                         int32_t len_offset, void* out, void* ws,
                                         size_t ws_bytes, void* stream) {
   CHECK(len_dev, STD_ERR_INVALID_ARGUMENT, "len_dev is null");
-  return dense_verify(s, q, n_q, kv, len_dev, len_offset, out, ws, ws_bytes, stream);
+  return dense_verify(s, q, n_q, 1, kv, len_dev, len_offset, out, ws, ws_bytes, stream);
+}
+
+size_t std_dense_verify_batch_workspace(const std_attn_shape_t* s, int32_t n_q, int32_t batch,
+                                        const std_kv_t* kv) {
+  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK || n_q < 1 || batch < 1 ||
+      (long long)batch * n_q * s->n_q_heads > (1 << 24))
+    return 0;
+  int chunk;
+  const int splits = dense_splits(s, kv, &chunk, batch);
+  return split_workspace(splits, batch * n_q * s->n_q_heads, s->head_dim).bytes();
+}
+
+std_status_t std_dense_verify_attn_batch(const std_attn_shape_t* s, const void* q, int32_t n_q,
+                                         int32_t batch, const std_kv_t* kv,
+                                         const int32_t* len_dev, int32_t len_offset, void* out,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  return dense_verify(s, q, n_q, batch, kv, len_dev, len_offset, out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- sparse draft
@@ -240,7 +274,7 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t bat
   AttnArgs a{};
   a.q = q; a.k = kv->k; a.v = kv->v; a.out = out;
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
-  a.capacity = kv->capacity; a.len = kv->len; a.n_q = batch; a.batch = batch;
+  a.capacity = kv->capacity; a.len = kv->len; a.n_q = 1; a.batch = batch;
   a.len_dev = len_dev; a.len_off = len_off;
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = true; a.idx = idx;
@@ -349,16 +383,27 @@ std_status_t std_select_topk(const std_attn_shape_t* s, const void* q_text, int3
 std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits, int32_t vocab,
                         std_dtype_t logits_dtype, int32_t* out_tokens, int32_t* n_out,
                         float* margins_or_null, int32_t* seq_len_inout_or_null, void* stream) {
+  return std_accept_batch(draft, gamma, 1, logits, vocab, logits_dtype, out_tokens, n_out,
+                          margins_or_null, seq_len_inout_or_null, stream);
+}
+
+std_status_t std_accept_batch(const int32_t* draft, int32_t gamma, int32_t batch,
+                              const void* logits, int32_t vocab, std_dtype_t logits_dtype,
+                              int32_t* out_tokens, int32_t* n_out, float* margins_or_null,
+                              int32_t* seq_len_inout_or_null, void* stream) {
   CHECK(gamma >= 0 && gamma < (1 << 20), STD_ERR_INVALID_ARGUMENT, "gamma %d out of range",
         gamma);
+  CHECK(batch >= 1 && (long long)batch * (gamma + 1) <= 0x7fffffffLL, STD_ERR_INVALID_ARGUMENT,
+        "need batch (%d) >= 1 and batch * (gamma + 1) rows to fit the grid", batch);
   CHECK(vocab >= 1, STD_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
   CHECK(gamma == 0 || draft, STD_ERR_INVALID_ARGUMENT, "draft is null");
   CHECK(logits && out_tokens && n_out, STD_ERR_INVALID_ARGUMENT,
         "logits / out_tokens / n_out is null");
   CHECK(logits_dtype == STD_DTYPE_F32 || logits_dtype == STD_DTYPE_BF16,
         STD_ERR_INVALID_ARGUMENT, "unknown logits dtype %d", (int)logits_dtype);
-  return hip_status(launch_accept(draft, gamma, logits, vocab, logits_dtype == STD_DTYPE_BF16,
-                                  out_tokens, n_out, margins_or_null, seq_len_inout_or_null,
+  return hip_status(launch_accept(draft, gamma, batch, logits, vocab,
+                                  logits_dtype == STD_DTYPE_BF16, out_tokens, n_out,
+                                  margins_or_null, seq_len_inout_or_null,
                                   static_cast<hipStream_t>(stream)));
 }
 

@@ -288,15 +288,22 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   constexpr int DB = D / 16;
   constexpr int CPR = D / 8;
   constexpr int TILE = 64 * D;                       // elements of one K or V tile
-  const int len = lsrc.get();
   constexpr int LPT = 64 * CPR / kDenseThreads;      // copies per thread per tensor per tile
   __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE + 64 * D];   // [buffer][K, V], Q
 
-  const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kh = wave & 1, nbw = wave >> 1;
   const int G = hq / hkv;
   const int Rg = n_q * G;
+  // grid z = (sequence, 64-row block); sequence b of a batch has its own
+  // queries, cache and length (one sequence: b = 0)
+  const int n_rb = (Rg + 63) / 64;
+  const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z % n_rb, b = blockIdx.z / n_rb;
+  q += (size_t)b * n_q * hq * D;
+  k += (size_t)b * hkv * capacity * D;
+  v += (size_t)b * hkv * capacity * D;
+  if (lsrc.dev) lsrc.dev += b;
+  const int len = lsrc.get();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kh = wave & 1, nbw = wave >> 1;
   const int col = lane & 15, grp = lane >> 4;
   const int r0 = rb * 64 + nbw * 16;                 // first query row of this wave
   const bool active = r0 < Rg;                       // wave-uniform
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   const float a0 = fast_exp2(m - Ms), a1 = fast_exp2(m1 - Ms);
   const float L = sum_over_groups(lsum * a0 + l1 * a1);
   if (!rok) return;
-  const size_t slot = (size_t)s * rows_total + (size_t)qi * hq + hh;
+  const size_t slot = (size_t)s * rows_total + ((size_t)b * n_q + qi) * hq + hh;
   if (grp == 0) ml[slot] = make_float2(M, L);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -732,7 +739,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 template <typename T>
 hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
-  const int rows = a.n_q * a.hq;
+  const int rows = (a.batch > 1 ? a.batch : 1) * a.n_q * a.hq;
   const auto* mlp = reinterpret_cast<const float2*>(a.ml);
   T* out = static_cast<T*>(a.out);
   if (a.d == 128)
@@ -766,12 +773,13 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
         q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
         a.topk, lsrc, a.splits, batch * a.hq, reinterpret_cast<float2*>(a.ml), a.o);
   } else {
+    const int batch = a.batch > 1 ? a.batch : 1;
     const int rows_group = a.n_q * (a.hq / a.hkv);
-    dim3 grid(a.splits, a.hkv, (rows_group + 63) / 64);
+    dim3 grid(a.splits, a.hkv, batch * ((rows_group + 63) / 64));
     dense_mfma_kernel<D><<<grid, kDenseThreads, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, lsrc,
                                                          a.n_q, c, a.splits,
                                                          reinterpret_cast<float2*>(a.ml), a.o,
-                                                         a.n_q * a.hq);
+                                                         batch * a.n_q * a.hq);
   }
   return hipGetLastError();
 }

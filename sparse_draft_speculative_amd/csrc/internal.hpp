@@ -80,8 +80,9 @@ struct AttnArgs {
   // (sparse batch: len_dev[b] for sequence b)
   const int32_t* len_dev;
   int len_off;
-  // sparse only: independent sequences laid out back to back (q, out
-  // [batch][Hq][D], K and V [batch][Hkv][capacity][D], idx [batch][Hkv][topk])
+  // independent sequences laid out back to back (q, out [batch][n_q][Hq][D],
+  // K and V [batch][Hkv][capacity][D], sparse idx [batch][Hkv][topk],
+  // len_dev[b]); 0 or 1: one sequence
   int batch;
   bool bf16;
   // sparse key list; for dense, sparse == false
@@ -118,7 +119,7 @@ size_t select_workspace_bytes(int hq, int hkv, int d, int n_text, int vis_len,
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
 // Acceptance (accept.hip).
-hipError_t launch_accept(const int32_t* draft, int gamma, const void* logits, int vocab,
+hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const void* logits, int vocab,
                          bool bf16, int32_t* out_tokens, int32_t* n_out, float* margins,
                          int32_t* seq_len, hipStream_t stream);
 

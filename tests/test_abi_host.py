@@ -214,6 +214,32 @@ def test_prefill_text_attn_rejects():
     assert lib.std_prefill_text_attn_workspace(ctypes.byref(sh), 100, 0) == 0
 
 
+def test_batched_verify_and_accept_reject():
+    lib = _lib.load()
+    E, U = _lib.STD_ERR_INVALID_ARGUMENT, _lib.STD_ERR_UNSUPPORTED
+    sh = _shape()
+    p = ctypes.c_void_p(FAKE)
+
+    def verify(batch=2, n_q=6, kv=None, q=p):
+        kv = kv if kv is not None else _kv()
+        return lib.std_dense_verify_attn_batch(ctypes.byref(sh), q, n_q, batch, ctypes.byref(kv),
+                                               None, 0, p, None, 0, None)
+    assert verify(batch=0) == E
+    assert verify(n_q=0) == E
+    assert verify(q=None) == E
+    assert verify(batch=70000) == E                       # rows past the grid
+    assert verify(kv=_kv(dtype=_lib.STD_DTYPE_F32)) == U
+    assert verify() == _lib.STD_ERR_WORKSPACE_TOO_SMALL    # valid: stops at the workspace
+    one = lib.std_dense_verify_workspace(ctypes.byref(sh), 6, ctypes.byref(_kv()))
+    two = lib.std_dense_verify_batch_workspace(ctypes.byref(sh), 6, 2, ctypes.byref(_kv()))
+    assert one > 0 and two > one
+    # acceptance: every check fires before a launch
+    assert lib.std_accept_batch(p, 3, 0, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept_batch(p, -1, 2, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept_batch(None, 3, 2, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept_batch(p, 3, 2, p, 10, 7, p, p, None, None, None) == E
+
+
 def test_check_idx_rejects():
     lib = _lib.load()
     E = _lib.STD_ERR_INVALID_ARGUMENT

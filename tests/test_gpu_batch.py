@@ -95,3 +95,85 @@ def test_batch_of_one_equals_single_call(lib):
                                         L, seq, 3, 0, vis_len, idx[0].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(a[0], b) and torch.equal(c[0], e)
+
+
+# ------------------------------------------------------- batched dense verify
+@pytest.mark.parametrize("B,hq,hkv,d,n_q,lens", [
+    (3, 28, 4, 128, 7, (2100, 1037, 2299)),
+    (4, 8, 2, 64, 5, (600, 517, 650, 701)),
+    (2, 32, 1, 128, 3, (4097, 4000)),          # G = 32: several 64-row blocks per sequence
+])
+def test_batched_dense_verify_matches_oracle(lib, B, hq, hkv, d, n_q, lens):
+    cap = max(lens) + 5
+    g = torch.Generator(device="cpu").manual_seed(B * 31 + hq)
+    k = torch.randn(B, hkv, cap, d, generator=g).bfloat16().cuda()
+    v = torch.randn(B, hkv, cap, d, generator=g).bfloat16().cuda()
+    q = (torch.randn(B, n_q, hq, d, generator=g) * 1.5).bfloat16().cuda()
+    len_dev = torch.tensor(lens, dtype=torch.int32, device="cuda") - 4     # offset 4 below
+    say(f"batched dense B={B} hq={hq} hkv={hkv} d={d} n_q={n_q} lens={lens}")
+    out = lib.std_dense_verify_attn_batch(q, k, v, max(lens), len_dev=len_dev, len_offset=4)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = oracle.dense_verify(f64(q[b]), f64(k[b]), f64(v[b]), lens[b])
+        assert np.max(np.abs(f64(out[b]) - ref)) <= TOL, b
+
+
+def test_batched_dense_verify_of_one_equals_single_call(lib):
+    g = torch.Generator(device="cpu").manual_seed(5)
+    k = torch.randn(1, 4, 3000, 128, generator=g).bfloat16().cuda()
+    v = torch.randn(1, 4, 3000, 128, generator=g).bfloat16().cuda()
+    q = torch.randn(1, 7, 28, 128, generator=g).bfloat16().cuda()
+    out_b = lib.std_dense_verify_attn_batch(q, k, v, 2999)
+    out_1 = lib.std_dense_verify_attn(q[0].contiguous(), k[0].contiguous(), v[0].contiguous(),
+                                      2999)
+    torch.cuda.synchronize()
+    assert torch.equal(out_b[0], out_1)
+
+
+# ------------------------------------------------------------ batched accept
+def test_batched_accept_matches_oracle(lib):
+    import synth
+    B, gamma, vocab = 5, 6, 3000
+    cases = [synth.accept_case(gamma, vocab, 0.8, seed=70 + b, dtype=torch.bfloat16,
+                               n_ties=b % 2) for b in range(B)]
+    draft = torch.stack([c[0] for c in cases]).cuda()
+    logits = torch.stack([c[1] for c in cases]).contiguous().cuda()
+    seq = torch.tensor([100 * b for b in range(B)], dtype=torch.int32, device="cuda")
+    toks, n_out = lib.std_accept_batch(draft, logits, seq_len=seq)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref_toks, ref_n, _, _ = oracle.accept(cases[b][0].numpy(), f64(cases[b][1]))
+        assert toks[b].cpu().numpy().tolist() == ref_toks.tolist(), b
+        assert int(n_out[b]) == ref_n
+        assert int(seq[b]) == 100 * b + ref_n
+
+
+# ----------------------------------------------------- one batched cycle
+def test_batched_cycle_equals_single_calls(lib):
+    """gamma draft steps for three sequences through the batched call equal
+    the single-sequence device-length calls with the same bound, bit for bit
+    (same kernel and split count, per-sequence offsets).  The batched verify
+    pass raises its split count so the grid fills whole rounds, which
+    changes the reduction order: it is held to the oracle instead."""
+    B, hq, hkv, d, vis_len, topk, gamma = 3, 28, 4, 128, 1500, 128, 4
+    ctx = (1700, 1601, 1800)
+    cap = max(ctx) + gamma + 2
+    q, k, v, idx = make_batch(B, hq, hkv, d, 0, vis_len, cap, topk, seed=99)
+    g = torch.Generator(device="cpu").manual_seed(98)
+    qv = (torch.randn(B, gamma + 1, hq, d, generator=g) * 1.5).bfloat16().cuda()
+    seq = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    max_len = cap
+    drafts_b = [lib.std_sparse_decode_attn_batch(q, k, v, max_len, 0, vis_len, idx, len_dev=seq,
+                                                 len_offset=1 + j) for j in range(gamma)]
+    verify_b = lib.std_dense_verify_attn_batch(qv, k, v, max_len, len_dev=seq,
+                                               len_offset=gamma + 1)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kb, vb = k[b].contiguous(), v[b].contiguous()
+        for j in range(gamma):
+            one = lib.std_sparse_decode_attn_dlen(q[b].contiguous(), kb, vb, max_len,
+                                                  seq[b:b + 1], 1 + j, 0, vis_len,
+                                                  idx[b].contiguous())
+            assert torch.equal(drafts_b[j][b], one), (b, j)
+        ref = oracle.dense_verify(f64(qv[b]), f64(kb), f64(vb), ctx[b] + gamma + 1)
+        assert np.max(np.abs(f64(verify_b[b]) - ref)) <= TOL, b
