@@ -63,6 +63,8 @@ def parse():
                     help="streams the per-layer selections are dealt over")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill text attention + selection measurement")
+    ap.add_argument("--batch-seqs", type=int, default=4,
+                    help="sequences in the batched decode-cycle measurement")
     ap.add_argument("--no-batch", action="store_true",
                     help="skip the batched sparse draft measurement")
     ap.add_argument("--no-prefill-lse", action="store_true",
@@ -380,6 +382,8 @@ def main():
                       "normalisers"}
 
     batch_sparse = None if args.no_batch else batched_sparse(sd, cfg, layers[0], idx[0], st)
+    batch_cycles = None if args.no_batch else batched_cycles(sd, cfg, layers, idx, st, pool,
+                                                             args.batch_seqs)
 
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
@@ -463,6 +467,7 @@ def main():
         "selection_prefill_lse": sel_prefill,
         "prefill_then_selection": pf,
         "batched_sparse": batch_sparse,
+        "batched_decode": batch_cycles,
         "hbm_read_probe": probe,
         "projection": projection(cycle_ms, G, dense_ms_per_tok),
     }
@@ -558,6 +563,90 @@ def batched_sparse(sd, cfg, lay, idx, st, batches=(1, 4, 16), reps=20):
                             "verify_frac": round(gbpsv * 1e9 / PEAK_HBM, 4)}
         del k, v, q, qv, ib, o, ov, ws, wsv
         torch.cuda.empty_cache()
+    return out
+
+
+def batched_cycles(sd, cfg, layers, idx, st, pool, B, cycles=24):
+    """Decode cycles for B sequences through the batched calls: per cycle
+    gamma x 28 batched draft launches, 28 batched verify launches and one
+    batched acceptance, captured as three graphs and replayed; every
+    sequence keeps its own device length, advanced by its own n + 1.  The
+    sequences are copies of the 28 c4 layers (distinct addresses), so the
+    bytes moved are B times a single sequence's."""
+    import torch
+    G, L = cfg.gamma, len(layers)
+    dev = layers[0]["k"].device
+    rep = lambda t: t[None].expand(B, *t.shape).contiguous()   # noqa: E731
+    kb = [rep(lay["k"]) for lay in layers]
+    vb = [rep(lay["v"]) for lay in layers]
+    qd = [[rep(lay["q_draft"][j]) for j in range(G)] for lay in layers]
+    qv = [rep(lay["q_verify"]) for lay in layers]
+    ib = [rep(t) for t in idx]
+    cap = cfg.capacity
+    shape = sd.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+    ws_s = torch.zeros(max(sd.std_sparse_decode_batch_workspace(shape, B, kb[0], cap,
+                                                                cfg.vis_start, cfg.vis_len,
+                                                                cfg.topk), 256),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.zeros(max(sd.std_dense_verify_batch_workspace(shape, G + 1, B, kb[0], cap), 256),
+                       dtype=torch.uint8, device=dev)
+    o_s = torch.empty_like(qd[0][0])
+    o_d = torch.empty_like(qv[0])
+    seq = torch.full((B,), cfg.ctx, dtype=torch.int32, device=dev)
+    draft = torch.stack([pool[b % len(pool)][0] for b in range(B)]).contiguous()
+    logits = torch.stack([pool[b % len(pool)][1] for b in range(B)]).contiguous()
+    toks = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
+    n_out = torch.zeros(B, dtype=torch.int32, device=dev)
+    total = torch.zeros(B, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def draft_phase():
+        for j in range(G):
+            for l in range(L):
+                sd.std_sparse_decode_attn_batch(qd[l][j], kb[l], vb[l], cap, cfg.vis_start,
+                                                cfg.vis_len, ib[l], len_dev=seq, len_offset=1 + j,
+                                                out=o_s, workspace=ws_s, stream=st)
+
+    def verify_phase():
+        for l in range(L):
+            sd.std_dense_verify_attn_batch(qv[l], kb[l], vb[l], cap, len_dev=seq,
+                                           len_offset=G + 1, out=o_d, workspace=ws_d, stream=st)
+
+    def accept():
+        sd.std_accept_batch(draft, logits, out_tokens=toks, n_out=n_out, seq_len=seq, stream=st)
+        total.add_(n_out)
+
+    with torch.cuda.stream(st):
+        draft_phase()
+        verify_phase()
+        accept()
+    torch.cuda.synchronize()
+    graphs = []
+    for fn in (draft_phase, verify_phase, accept):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        seq.fill_(cfg.ctx)
+        total.zero_()
+        e0.record()
+        for _ in range(cycles):
+            for g in graphs:
+                g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    emitted = int(total.sum().item())
+    out = {"sequences": B, "cycles": cycles, "ms_per_cycle": round(ms / cycles, 4),
+           "tokens_emitted": emitted,
+           "decode_tokens_per_s": round(emitted / (ms * 1e-3), 1),
+           "note": "28 c4 layers per sequence, gamma draft steps + verify + acceptance per "
+                   "cycle for all B sequences, selection not included"}
+    del kb, vb, qd, qv, ib, ws_s, ws_d, graphs
+    torch.cuda.empty_cache()
     return out
 
 
