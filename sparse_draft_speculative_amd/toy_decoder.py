@@ -1,4 +1,4 @@
-"""End-to-end driver: a small decoder whose attention runs on the four calls.
+"""End-to-end example: a small decoder whose attention runs on the four calls.
 
 The decoder is a standard pre-norm transformer (RMSNorm, rotary position
 embedding with the rotate-half pairing, grouped-query attention, SwiGLU MLP,
