@@ -38,9 +38,11 @@
  * - stream is a hipStream_t passed as void*; NULL means the default stream.
  * - Workspace: each call that needs scratch takes a caller-allocated device
  *   buffer of at least the size its *_workspace query returns (256-byte
- *   aligned).  Its contents need no initialisation and are garbage after
- *   the call.  A workspace serves one call at a time: two calls in flight at
- *   once (on different streams) need two workspaces.
+ *   aligned).  A query returns 0 when its arguments fail a check that its
+ *   call makes on them (std_last_error() then names it).  The buffer's
+ *   contents need no initialisation and are garbage after the call.  A
+ *   workspace serves one call at a time: two calls in flight at once (on
+ *   different streams) need two workspaces.
  */
 #ifndef STDSPEC_H
 #define STDSPEC_H

@@ -124,6 +124,44 @@ std_status_t check_ws(void* ws, size_t have, size_t need) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Checks of the dense verify call that need no device pointer (its
+// workspace queries apply them too).
+std_status_t check_dense(const std_attn_shape_t* s, const std_kv_t* kv, int32_t n_q,
+                         int32_t batch) {
+  TRY(check_shape(s));
+  TRY(check_kv(kv, false));
+  TRY(check_extent(s, kv));
+  CHECK(n_q >= 1 && n_q <= kv->len, STD_ERR_INVALID_ARGUMENT, "need 1 <= n_q (%d) <= len (%d)",
+        n_q, kv->len);
+  CHECK(batch >= 1 && (long long)batch * n_q * s->n_q_heads <= (1 << 24),
+        STD_ERR_INVALID_ARGUMENT, "need batch (%d) >= 1 and batch * n_q * n_q_heads <= 2^24",
+        batch);
+  if (batch > 1) {
+    const long long n_rb = ((long long)n_q * (s->n_q_heads / s->n_kv_heads) + 63) / 64;
+    CHECK(kv->dtype == STD_DTYPE_BF16, STD_ERR_UNSUPPORTED, "batched dense verify needs bf16 KV");
+    CHECK(batch * n_rb <= 65535, STD_ERR_INVALID_ARGUMENT,
+          "batch * row blocks (%lld) exceeds the grid", batch * n_rb);
+  }
+  return ok();
+}
+
+// The same for the sparse draft call.
+std_status_t check_sparse_call(const std_attn_shape_t* s, const std_kv_t* kv, std_vis_t vis,
+                               int32_t topk, int32_t batch) {
+  TRY(check_shape(s));
+  TRY(check_kv(kv, false));
+  TRY(check_extent(s, kv));
+  TRY(check_sparse(s, kv, vis, topk));
+  CHECK(batch >= 1 && batch <= 65535 && (long long)batch * s->n_q_heads <= (1 << 24),
+        STD_ERR_INVALID_ARGUMENT, "need 1 <= batch (%d) <= 65535 and batch * n_q_heads <= 2^24",
+        batch);
+  if (batch > 1) {
+    CHECK(kv->dtype == STD_DTYPE_BF16 && s->n_q_heads / s->n_kv_heads <= 16,
+          STD_ERR_UNSUPPORTED, "batched sparse decode needs bf16 KV and G <= 16");
+  }
+  return ok();
+}
+
 }  // namespace
 
 namespace stdspec {
@@ -154,7 +192,7 @@ const char* std_last_error(void) { return g_err; }
 
 // ---------------------------------------------------------------- dense verify
 size_t std_dense_verify_workspace(const std_attn_shape_t* s, int32_t n_q, const std_kv_t* kv) {
-  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK || n_q < 1) return 0;
+  if (check_dense(s, kv, n_q, 1) != STD_OK) return 0;
   int chunk;
   const int splits = dense_splits(s, kv, &chunk);
   return split_workspace(splits, n_q * s->n_q_heads, s->head_dim).bytes();
@@ -167,23 +205,11 @@ namespace {
 std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q, int32_t batch,
                           const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
                           void* out, void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_shape(s));
+  TRY(check_dense(s, kv, n_q, batch));
   TRY(check_kv(kv, true));
-  TRY(check_extent(s, kv));
   CHECK(q && out, STD_ERR_INVALID_ARGUMENT, "q / out is null");
-  CHECK(n_q >= 1 && n_q <= kv->len, STD_ERR_INVALID_ARGUMENT, "need 1 <= n_q (%d) <= len (%d)",
-        n_q, kv->len);
-  CHECK(batch >= 1 && (long long)batch * n_q * s->n_q_heads <= (1 << 24),
-        STD_ERR_INVALID_ARGUMENT, "need batch (%d) >= 1 and batch * n_q * n_q_heads <= 2^24",
-        batch);
   CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
         STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
-  if (batch > 1) {
-    const long long n_rb = ((long long)n_q * (s->n_q_heads / s->n_kv_heads) + 63) / 64;
-    CHECK(kv->dtype == STD_DTYPE_BF16, STD_ERR_UNSUPPORTED, "batched dense verify needs bf16 KV");
-    CHECK(batch * n_rb <= 65535, STD_ERR_INVALID_ARGUMENT,
-          "batch * row blocks (%lld) exceeds the grid", batch * n_rb);
-  }
   int chunk;
   const int splits = dense_splits(s, kv, &chunk, batch);
   const SplitWorkspace w = split_workspace(splits, batch * n_q * s->n_q_heads, s->head_dim);
@@ -221,9 +247,7 @@ std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* s, const void* q
 
 size_t std_dense_verify_batch_workspace(const std_attn_shape_t* s, int32_t n_q, int32_t batch,
                                         const std_kv_t* kv) {
-  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK || n_q < 1 || batch < 1 ||
-      (long long)batch * n_q * s->n_q_heads > (1 << 24))
-    return 0;
+  if (check_dense(s, kv, n_q, batch) != STD_OK) return 0;
   int chunk;
   const int splits = dense_splits(s, kv, &chunk, batch);
   return split_workspace(splits, batch * n_q * s->n_q_heads, s->head_dim).bytes();
@@ -239,9 +263,7 @@ std_status_t std_dense_verify_attn_batch(const std_attn_shape_t* s, const void* 
 // ---------------------------------------------------------------- sparse draft
 size_t std_sparse_decode_workspace(const std_attn_shape_t* s, const std_kv_t* kv, std_vis_t vis,
                                    int32_t topk) {
-  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK ||
-      check_sparse(s, kv, vis, topk) != STD_OK)
-    return 0;
+  if (check_sparse_call(s, kv, vis, topk, 1) != STD_OK) return 0;
   return split_workspace(sparse_splits(kv, vis, topk), s->n_q_heads, s->head_dim).bytes();
 }
 
@@ -253,21 +275,12 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t bat
                            const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
                            std_vis_t vis, const int32_t* idx, int32_t topk, void* out, void* ws,
                            size_t ws_bytes, void* stream) {
-  TRY(check_shape(s));
+  TRY(check_sparse_call(s, kv, vis, topk, batch));
   TRY(check_kv(kv, true));
-  TRY(check_extent(s, kv));
-  TRY(check_sparse(s, kv, vis, topk));
   CHECK(q && out, STD_ERR_INVALID_ARGUMENT, "q / out is null");
   CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
   CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
         STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
-  CHECK(batch >= 1 && batch <= 65535 && (long long)batch * s->n_q_heads <= (1 << 24),
-        STD_ERR_INVALID_ARGUMENT, "need 1 <= batch (%d) <= 65535 and batch * n_q_heads <= 2^24",
-        batch);
-  if (batch > 1) {
-    CHECK(kv->dtype == STD_DTYPE_BF16 && s->n_q_heads / s->n_kv_heads <= 16,
-          STD_ERR_UNSUPPORTED, "batched sparse decode needs bf16 KV and G <= 16");
-  }
   const int splits = sparse_splits(kv, vis, topk);
   const SplitWorkspace w = split_workspace(splits, batch * s->n_q_heads, s->head_dim);
   TRY(check_ws(ws, ws_bytes, w.bytes()));
@@ -307,9 +320,7 @@ std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* 
 
 size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* s, int32_t batch,
                                          const std_kv_t* kv, std_vis_t vis, int32_t topk) {
-  if (check_shape(s) != STD_OK || check_kv(kv, false) != STD_OK ||
-      check_sparse(s, kv, vis, topk) != STD_OK || batch < 1 || batch > 65535)
-    return 0;
+  if (check_sparse_call(s, kv, vis, topk, batch) != STD_OK) return 0;
   return split_workspace(sparse_splits(kv, vis, topk), batch * s->n_q_heads, s->head_dim)
       .bytes();
 }
@@ -346,7 +357,11 @@ static std_status_t check_select(const std_attn_shape_t* s, int32_t text_start, 
 
 size_t std_select_topk_workspace(const std_attn_shape_t* s, int32_t n_text, std_vis_t vis,
                                  int32_t topk, const std_kv_t* kv) {
-  if (!kv || check_shape(s) != STD_OK) return 0;
+  if (!kv) {
+    fail(STD_ERR_INVALID_ARGUMENT, "kv is null");
+    return 0;
+  }
+  if (check_shape(s) != STD_OK) return 0;
   const int text_start = vis.vis_start + vis.vis_len;  // earliest legal start
   const int ts = kv->len - n_text > text_start ? kv->len - n_text : text_start;
   if (check_select(s, ts, n_text, kv, vis, topk) != STD_OK) return 0;
@@ -411,7 +426,12 @@ std_status_t std_accept_batch(const int32_t* draft, int32_t gamma, int32_t batch
 
 size_t std_prefill_text_attn_workspace(const std_attn_shape_t* s, int32_t text_start,
                                        int32_t n_text) {
-  if (check_shape(s) != STD_OK || text_start < 0 || n_text < 1) return 0;
+  if (check_shape(s) != STD_OK) return 0;
+  if (text_start < 0 || n_text < 1) {
+    fail(STD_ERR_INVALID_ARGUMENT, "need text_start (%d) >= 0 and n_text (%d) >= 1", text_start,
+         n_text);
+    return 0;
+  }
   return prefill_workspace_bytes(s->n_q_heads, s->head_dim, text_start, n_text);
 }
 

@@ -286,3 +286,39 @@ def test_workspace_sizes():
     assert w >= 4 * 140000 * 4                 # room for the scores
     assert lib.std_select_topk_workspace(ctypes.byref(sh), 2048, _lib.Vis(0, 140000), 0,
                                          ctypes.byref(_kv(142048, 142048))) == 0
+
+
+def test_workspace_queries_follow_their_calls():
+    """A query returns 0, with the reason in std_last_error, for arguments its
+    call rejects before the workspace check (batched limits and dtypes too)."""
+    lib = _lib.load()
+    sh = _shape()
+    f32 = _kv(dtype=_lib.STD_DTYPE_F32)
+    vis = _lib.Vis(0, 800)
+
+    def reason():
+        return lib.std_last_error().decode()
+
+    # dense verify: n_q past the length; batch > 1 needs bf16
+    assert lib.std_dense_verify_workspace(ctypes.byref(sh), 1001, ctypes.byref(_kv())) == 0
+    assert "n_q" in reason()
+    assert lib.std_dense_verify_batch_workspace(ctypes.byref(sh), 6, 2, ctypes.byref(f32)) == 0
+    assert "bf16" in reason()
+    assert lib.std_dense_verify_batch_workspace(ctypes.byref(sh), 6, 1, ctypes.byref(f32)) > 0
+    assert lib.std_dense_verify_batch_workspace(ctypes.byref(sh), 6, 70000,
+                                                ctypes.byref(_kv())) == 0
+    # sparse draft: batch > 1 needs bf16; batch * n_q_heads bounded
+    assert lib.std_sparse_decode_batch_workspace(ctypes.byref(sh), 2, ctypes.byref(f32), vis,
+                                                 64) == 0
+    assert "bf16" in reason()
+    assert lib.std_sparse_decode_batch_workspace(ctypes.byref(sh), 1, ctypes.byref(f32), vis,
+                                                 64) > 0
+    big = _shape(hq=512, hkv=32)
+    assert lib.std_sparse_decode_batch_workspace(ctypes.byref(big), 40000, ctypes.byref(_kv()),
+                                                 vis, 64) == 0
+    assert "2^24" in reason()
+    # selection and prefill queries name their reason too
+    assert lib.std_select_topk_workspace(ctypes.byref(sh), 16, vis, 64, None) == 0
+    assert "kv is null" in reason()
+    assert lib.std_prefill_text_attn_workspace(ctypes.byref(sh), -1, 10) == 0
+    assert "text_start" in reason()
