@@ -24,7 +24,9 @@ Non-attention model work (projections, MLP, LM head) is outside the path.
 
 value = new tokens per second of the whole request (selection included).
 Also reported: dense-only decoding tokens/s (the same dense kernel with one
-query per token, no selection), per-kernel HBM GB/s and % of 8 TB/s.
+query per token, no selection), per-kernel HBM GB/s and % of 8 TB/s, and the
+attention bytes per emitted token (measured, and projected per acceptance
+rate against a dense decode step).
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -461,6 +463,8 @@ def main():
         "phases_ms_per_step": {k: round(v / args.steps, 3) for k, v in
                                {**phases, "accept": ph["accept_ms"]}.items()},
         "accepted_tokens_per_cycle": round(ph["emitted"] / max(cycles, 1), 3),
+        "attn_mb_per_emitted_token": round((ph["sparse_bytes"] + ph["dense_bytes"])
+                                           / max(ph["emitted"], 1) / 1e6, 1),
         "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
         "dense_only_attn_gbps": round(dense_gbps, 1),
         "cycle_ms": cycle_stats(cycle_ms),
@@ -469,7 +473,10 @@ def main():
         "batched_sparse": batch_sparse,
         "batched_decode": batch_cycles,
         "hbm_read_probe": probe,
-        "projection": projection(cycle_ms, G, dense_ms_per_tok),
+        "projection": projection(cycle_ms, G, dense_ms_per_tok,
+                                 L * attn_bytes_sparse(cfg, cfg.ctx + 1),
+                                 L * attn_bytes_dense(cfg, cfg.verify_len, G + 1),
+                                 L * attn_bytes_dense(cfg, cfg.ctx + 1, 1)),
     }
     if not args.no_toy:
         line["toy_e2e"] = toy_e2e()
@@ -677,19 +684,32 @@ def cycle_stats(ms):
             "p90": round(q(0.9), 4)}
 
 
-def projection(cycle_ms, gamma, dense_ms_per_tok):
+def projection(cycle_ms, gamma, dense_ms_per_tok, step_bytes, verify_bytes, dense_tok_bytes):
     """Attention-only decode rate projected from the measured median cycle
     time: E(alpha) = (1 - alpha^(gamma+1)) / (1 - alpha) tokens per cycle
     under independent per-token acceptance, for alpha in {0.8, 0.9, 0.95},
-    against dense-only decoding (selection not included)."""
+    against dense-only decoding (selection not included).
+
+    Beside it, the attention I/O per emitted token (the pages' I/O argument:
+    drafting reads only the kept KV, so once acceptance is high a token
+    costs fewer bytes than a dense decode step; technical summary, Main
+    contributions).  The pages print no formula; the reading used here is a
+    cycle's algorithmic bytes, gamma draft steps (step_bytes each, all
+    layers) plus one verify pass (verify_bytes), over E(alpha), against
+    dense_tok_bytes for one dense decode step."""
     t = cycle_ms[len(cycle_ms) // 2]
+    cycle_bytes = gamma * step_bytes + verify_bytes
     out = {"label": "attention-only, projected", "t_cycle_ms": round(t, 4),
-           "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2)}
+           "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
+           "dense_mb_per_token": round(dense_tok_bytes / 1e6, 1),
+           "cycle_mb": round(cycle_bytes / 1e6, 1)}
     for a in (0.8, 0.9, 0.95):
         e = (1 - a ** (gamma + 1)) / (1 - a)
         out[f"alpha_{a}"] = {"tokens_per_cycle": round(e, 3),
                              "tokens_per_s": round(e * 1e3 / t, 1),
-                             "speedup_vs_dense": round(e * dense_ms_per_tok / t, 3)}
+                             "speedup_vs_dense": round(e * dense_ms_per_tok / t, 3),
+                             "mb_per_token": round(cycle_bytes / e / 1e6, 1),
+                             "io_reduction_vs_dense": round(dense_tok_bytes * e / cycle_bytes, 3)}
     return out
 
 
