@@ -105,7 +105,7 @@ def select_flops(cfg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); this build has no "
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
