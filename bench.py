@@ -14,8 +14,10 @@ One step = one request through the whole hot path:
   (b) gamma sparse draft steps x 28 layers (std_sparse_decode_attn),
   (c) one dense verify pass x 28 layers with gamma+1 queries
       (std_dense_verify_attn),
-  (d) greedy acceptance (std_accept), whose n_out is read back to advance
-      the cache length.
+  (d) greedy acceptance (std_accept), which advances the device-resident
+      cache length by n + 1; n_out is copied to pinned host memory without
+      a wait and read one cycle later, so the host only counts tokens while
+      the GPU runs the next cycle (no per-cycle host round trip).
 The acceptance step sees synthetic draft tokens and logits (vocab 152,064)
 in which each draft agrees with the dense argmax with probability
 alpha = 0.95 (the pages report that top-K KV keeps the original prediction
@@ -73,6 +75,9 @@ def parse():
                     help="skip the selection timing with a caller-supplied row LSE")
     ap.add_argument("--no-toy", action="store_true",
                     help="skip the end-to-end toy decoder measurement")
+    ap.add_argument("--sync-each-cycle", action="store_true",
+                    help="read each cycle's n_out before launching the next (the blocking "
+                         "loop, for comparison)")
     return ap.parse_args()
 
 
@@ -252,10 +257,21 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    # n_out of each cycle lands in pinned host memory by an asynchronous copy
+    # on the bench stream; the host reads it one cycle late (after launching
+    # the next cycle), so the GPU never waits for the host between cycles.
+    # A cycle is launched only while the tokens it could add are certainly
+    # still needed: known tokens + (cycles in flight) x (gamma + 1) < target,
+    # so no cycle is ever wasted; the host waits only for the oldest cycle
+    # in flight, and only once no further cycle is certainly needed.
+    RING = 64
+    n_host = torch.zeros(RING, dtype=torch.int32, pin_memory=True)
+
     def run_request(timing):
         """One request; returns (new tokens, cycles, phase times ms or None)."""
         e_sel = (ev(), ev())
         cyc_ev = []
+        inflight = []                      # (ring slot, copy-done event)
         with torch.cuda.stream(st):
             e_sel[0].record()
             select_all()
@@ -266,28 +282,41 @@ def main():
             cycles = 0
             emitted = 0
             sp_bytes = dv_bytes = 0
-            while produced < args.new_tokens:
-                es = (ev(), ev(), ev(), ev())
-                es[0].record()
-                run_draft()
-                es[1].record()
-                run_verify()
-                es[2].record()
-                run_accept[cycles % len(run_accept)]()
-                es[3].record()
-                cyc_ev.append(es)
+            while produced < args.new_tokens or inflight:
+                if (produced + len(inflight) * (G + 1) < args.new_tokens
+                        and len(inflight) < RING):
+                    es = (ev(), ev(), ev(), ev())
+                    es[0].record()
+                    run_draft()
+                    es[1].record()
+                    run_verify()
+                    es[2].record()
+                    run_accept[cycles % len(run_accept)]()
+                    es[3].record()
+                    cyc_ev.append(es)
+                    slot = cycles % RING
+                    n_host[slot:slot + 1].copy_(n_out, non_blocking=True)
+                    done = torch.cuda.Event()
+                    done.record(st)
+                    inflight.append((slot, done))
+                    cycles += 1
+                    if not args.sync_each_cycle:
+                        continue
+                slot, done = inflight.pop(0)
+                done.synchronize()
+                n = int(n_host[slot])      # token count only; the device length is advanced
                 sp_bytes += sum(L * attn_bytes_sparse(cfg, t + 1 + j) for j in range(G))
                 dv_bytes += L * attn_bytes_dense(cfg, t + G + 1, G + 1)
-                n = int(n_out.item())      # host sync: only to count the tokens
                 emitted += n
                 produced += n
                 t += n
-                cycles += 1
         torch.cuda.synchronize()
         ph = None
         if timing:
             ph = {"select_ms": e_sel[0].elapsed_time(e_sel[1]),
                   "cycle_ms": [a.elapsed_time(d) for a, _, _, d in cyc_ev],
+                  "gap_ms": [cyc_ev[i][3].elapsed_time(cyc_ev[i + 1][0])
+                             for i in range(len(cyc_ev) - 1)],
                   "draft_ms": sum(a.elapsed_time(b) for a, b, _, _ in cyc_ev),
                   "verify_ms": sum(b.elapsed_time(c) for _, b, c, _ in cyc_ev),
                   "accept_ms": sum(c.elapsed_time(d) for _, _, c, d in cyc_ev),
@@ -304,7 +333,9 @@ def main():
     new_tok = sum(r[0] for r in results)
     cycles = sum(r[1] for r in results)
     cycle_ms = sorted(x for r in results for x in r[2]["cycle_ms"])
-    ph = {k: sum(r[2][k] for r in results) for k in results[0][2] if k != "cycle_ms"}
+    gap_ms = sorted(x for r in results for x in r[2]["gap_ms"])
+    ph = {k: sum(r[2][k] for r in results) for k in results[0][2]
+          if k not in ("cycle_ms", "gap_ms")}
 
     # selection with the row normaliser (step 1) supplied by the caller, as
     # a prefill attention kernel returns it; the LSE itself is computed here
@@ -468,6 +499,9 @@ def main():
         "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
         "dense_only_attn_gbps": round(dense_gbps, 1),
         "cycle_ms": cycle_stats(cycle_ms),
+        "inter_cycle_gap_ms": cycle_stats(gap_ms),
+        "host_read_per_cycle": "blocking" if args.sync_each_cycle else
+                               "asynchronous, one cycle late",
         "selection_prefill_lse": sel_prefill,
         "prefill_then_selection": pf,
         "batched_sparse": batch_sparse,
@@ -771,13 +805,12 @@ def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
 
     for g in gammas:
         out["std"][f"gamma{g}"] = run(idx, g)
-    # Comparator: the same draft kernel over a static visual set -- the first
-    # STREAM_SINK visual positions and the last topk - STREAM_SINK ones -- in
-    # place of the attention-ranked top-K (sizes are this harness's choice).
+    # Comparator: the same draft kernel over the streaming lists
+    # (std_static_window_idx: the first STREAM_SINK visual positions and the
+    # last topk - STREAM_SINK) in place of the attention-ranked top-K (sizes
+    # are this harness's choice; the pages give none).
     topk = cfg["topk"]
-    fixed = torch.cat([torch.arange(STREAM_SINK), torch.arange(n_vis - (topk - STREAM_SINK), n_vis)])
-    static = [fixed.to(torch.int32).repeat(cfg["n_kv_heads"], 1).contiguous().cuda()
-              for _ in range(cfg["n_layers"])]
+    static = dec.select_static(0, n_vis, STREAM_SINK, topk)
     out["static_window"] = {"sink": STREAM_SINK, "window": topk - STREAM_SINK,
                             "std": {f"gamma{g}": run(static, g) for g in gammas}}
     return out

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define STD_ABI_VERSION 1
+#define STD_ABI_VERSION 2
 
 typedef enum {
   STD_OK = 0,
@@ -193,13 +193,16 @@ std_status_t std_dense_verify_attn(const std_attn_shape_t* shape, const void* q,
  * device memory lets a caller capture a whole cycle once (for example in a
  * HIP graph) and replay it with no host round trip.  These calls read the
  * valid length when their kernels run:
- *     len = min(max(*len_dev + len_offset, 1), kv->len)
- * kv->len is the upper bound: it sizes the launch and the workspace (query
- * the *_workspace functions with it), and every other argument, check and
- * result is that of the host-length call with this len.  The caller keeps
- * len >= vis_start + vis_len (sparse) and len >= n_q (dense); outside that
- * range the result is unspecified but every access stays inside the cache.
- * len_dev is an int32 device pointer, e.g. the seq_len std_accept advances.
+ *     len = min(max(*len_dev + len_offset, lo), kv->len)
+ * where lo is the shortest length the call is defined for: n_q (dense: every
+ * query row sees at least one key); vis_start + vis_len (sparse: the query
+ * follows the visual span), plus one when vis_start + topk == 0 (so the key
+ * list is never empty).  A device value below lo is raised to it, so the
+ * result is always a defined attention output.  kv->len is the upper bound:
+ * it sizes the launch and the workspace (query the *_workspace functions
+ * with it), and every other argument, check and result is that of the
+ * host-length call with this len.  len_dev is an int32 device pointer, e.g.
+ * the seq_len std_accept advances.
  * ------------------------------------------------------------------------ */
 std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* shape, const void* q,
                                          const std_kv_t* kv, const int32_t* len_dev,
@@ -220,11 +223,19 @@ std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* shape, const voi
  * back, K and V [batch][n_kv_heads][kv->capacity][head_dim] (kv->k, kv->v
  * point at sequence 0); idx [batch][n_kv_heads][topk], each list as in (b).
  * kv->len bounds every sequence's length and sizes the launch; sequence b
- * uses min(max(len_dev[b] + len_offset, 1), kv->len) when len_dev (batch
- * int32 in device memory) is given, else kv->len.  All sequences share vis
- * and topk.  bf16 KV with n_q_heads / n_kv_heads <= 16 only
- * (STD_ERR_UNSUPPORTED otherwise); 1 <= batch <= 65535.  With batch == 1
- * the result equals std_sparse_decode_attn(_dlen) bit for bit.
+ * uses min(max(len_dev[b] + len_offset, lo), kv->len) (lo as for the
+ * device-length calls) when len_dev (batch int32 in device memory) is
+ * given, else kv->len.  All sequences share vis and topk.  bf16 KV with
+ * n_q_heads / n_kv_heads <= 16 only (STD_ERR_UNSUPPORTED otherwise);
+ * 1 <= batch <= 65535.  With batch == 1 the result equals
+ * std_sparse_decode_attn(_dlen) bit for bit.
+ *
+ * Per-sequence draft lengths (Methodology item 3 defines the cycle per
+ * sequence: each drafts its own gamma tokens): gamma_dev_or_null is NULL
+ * (every sequence drafts in this step) or [batch] int32 device, and the
+ * call is draft step `step` (0-based) of a cycle: sequence b takes part only
+ * while step < gamma_dev[b]; for the others nothing is read and out[b] is
+ * left as it was.  step >= 0 when gamma_dev_or_null is given.
  * ------------------------------------------------------------------------ */
 size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* shape, int32_t batch,
                                          const std_kv_t* kv, std_vis_t vis, int32_t topk);
@@ -232,6 +243,7 @@ std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* shape, const v
                                           int32_t batch, const std_kv_t* kv,
                                           const int32_t* len_dev, int32_t len_offset,
                                           std_vis_t vis, const int32_t* idx, int32_t topk,
+                                          const int32_t* gamma_dev_or_null, int32_t step,
                                           void* out, void* workspace, size_t workspace_bytes,
                                           void* stream);
 
@@ -245,7 +257,12 @@ std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* shape, const v
  * kv   kv->k, kv->v point at [batch][n_kv_heads][capacity][head_dim];
  *      kv->len is the bound every sequence's length is clamped to.
  * len_dev  NULL (every sequence has length kv->len) or [batch] int32
- *      device: sequence b uses min(max(len_dev[b] + len_offset, 1), kv->len).
+ *      device: sequence b uses min(max(len_dev[b] + len_offset, n_q),
+ *      kv->len).
+ * A batch whose sequences draft different numbers of tokens verifies with
+ * n_q = 1 + the largest gamma: sequence b's rows 0..gamma_b are its verify
+ * rows (row i sees only keys up to its own position, so the rows after
+ * them change nothing in them) and std_accept_batch reads only those.
  * bf16 only for batch > 1 (fp32: STD_ERR_UNSUPPORTED); batch = 1 is
  * std_dense_verify_attn(_dlen) bit for bit.  With batch > 1 the key split
  * count is raised so the grid fills whole rounds of the machine, which can
@@ -284,15 +301,23 @@ std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
                         int32_t* n_out, float* margins_or_null,
                         int32_t* seq_len_inout_or_null, void* stream);
 
-/* (d, batched) Acceptance for `batch` sequences with the same gamma, each as
- * std_accept: draft [batch][gamma], logits [batch][gamma+1][vocab],
- * out_tokens [batch][gamma+1], n_out [batch], margins [batch][gamma+1] or
- * NULL, seq_len [batch] or NULL (sequence b's length advances by its own
- * n + 1).  batch = 1 is std_accept. */
+/* (d, batched) Acceptance for `batch` sequences, each as std_accept (the
+ * cycle of Methodology item 3 runs per sequence): draft [batch][gamma],
+ * logits [batch][gamma+1][vocab], out_tokens [batch][gamma+1], n_out
+ * [batch], margins [batch][gamma+1] or NULL, seq_len [batch] or NULL
+ * (sequence b's length advances by its own n + 1).
+ * gamma_dev_or_null: NULL (every sequence drafted gamma tokens) or [batch]
+ * int32 device holding each sequence's own draft length gamma_b, clamped
+ * into [0, gamma]; gamma is then the row stride of draft, logits and
+ * out_tokens.  Sequence b reads draft[b][0..gamma_b) and logit rows
+ * [b][0..gamma_b] only; n_b <= gamma_b; out_tokens[b][0..n_b] = its
+ * predictions, -1 in the remaining slots up to gamma; margins of rows past
+ * gamma_b are NaN.  batch = 1 with NULL is std_accept. */
 std_status_t std_accept_batch(const int32_t* draft, int32_t gamma, int32_t batch,
-                              const void* logits, int32_t vocab, std_dtype_t logits_dtype,
-                              int32_t* out_tokens, int32_t* n_out, float* margins_or_null,
-                              int32_t* seq_len_inout_or_null, void* stream);
+                              const int32_t* gamma_dev_or_null, const void* logits, int32_t vocab,
+                              std_dtype_t logits_dtype, int32_t* out_tokens, int32_t* n_out,
+                              float* margins_or_null, int32_t* seq_len_inout_or_null,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * Prefill attention of the text rows, returning their normalisers.
@@ -344,6 +369,28 @@ std_status_t std_prefill_text_attn(const std_attn_shape_t* shape, const void* q_
  * ------------------------------------------------------------------------ */
 std_status_t std_check_idx(const int32_t* idx, int32_t n_kv_heads, int32_t topk, std_vis_t vis,
                            int32_t* bad_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Index lists of the streaming-attention comparator.
+ *
+ * The pages compare StD with a streaming-attention draft that accepts fewer
+ * drafts (technical summary, Experimental results).  Such a policy keeps a
+ * few initial "sink" positions and a window of the most recent ones instead
+ * of ranking positions by attention.  Applied to the visual span only (the
+ * text KV stays whole, as in the StD draft), it is a fixed index list for
+ * the sparse draft calls; this call writes it:
+ *   idx_out[g] = vis_start + 0 .. vis_start + s - 1,
+ *                vis_start + vis_len - (topk - s) .. vis_start + vis_len - 1
+ * with s = min(sink, topk), the same for every KV head g, ascending and
+ * distinct (topk <= vis_len), i.e. a valid list for std_sparse_decode_attn.
+ * The pages give no sink or window size; the caller chooses them.
+ *
+ * idx_out  [n_kv_heads][topk] int32 device.  topk = 0 writes nothing.
+ * Errors: STD_ERR_INVALID_ARGUMENT before any launch for n_kv_heads < 1, a
+ * bad span, topk outside [0, vis_len], sink < 0 or a null idx_out.
+ * ------------------------------------------------------------------------ */
+std_status_t std_static_window_idx(int32_t n_kv_heads, std_vis_t vis, int32_t sink, int32_t topk,
+                                   int32_t* idx_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Streaming-read probe (measurement harness; no step of the method).

@@ -14,6 +14,9 @@ float64, slow and direct, so it can be checked against the pages by eye:
 * ``select_topk``   -- prefill-time top-K visual KV selection from the mean
                        text->visual attention score (technical summary,
                        Methodology item 4 "KV cache selection").
+* ``static_window_idx`` -- the visual positions a streaming-attention draft
+                       keeps (an attention sink plus a recent window), the
+                       comparator the pages' Experimental results name.
 * ``sparse_decode`` -- the sparse model's single-query attention over the
                        selected visual KV plus all non-visual KV (technical
                        summary, Methodology item 2, sparse model M_s).
@@ -38,11 +41,11 @@ the acceptance rule and the losslessness invariant of the toy loop.
 """
 
 from .attention import dense_verify, sparse_decode, sparse_key_set, attend, row_lse
-from .selection import select_topk, selection_scores, rank_topk
+from .selection import select_topk, selection_scores, rank_topk, static_window_idx
 from .acceptance import accept, argmax_margin
 
 __all__ = [
     "dense_verify", "sparse_decode", "sparse_key_set", "attend", "row_lse",
-    "select_topk", "selection_scores", "rank_topk",
+    "select_topk", "selection_scores", "rank_topk", "static_window_idx",
     "accept", "argmax_margin",
 ]

@@ -96,3 +96,26 @@ def select_topk(q_text, k, text_start, vis_start, vis_len, topk, scale=None):
     scores = selection_scores(q_text, k, text_start, vis_start, vis_len, scale)
     idx = np.stack([rank_topk(scores[g], topk) for g in range(scores.shape[0])])
     return idx + vis_start, scores
+
+
+def static_window_idx(vis_start, vis_len, sink, topk):
+    """Visual positions kept by the streaming-attention comparator.
+
+    The pages compare StD with a streaming-attention draft (technical
+    summary, Experimental results) without stating its sizes.  Reading: such
+    a policy keeps the first ``sink`` positions of the visual span (the
+    attention sink) and, for the rest of a budget of ``topk`` positions, the
+    most recent ones (the window); the text KV is kept whole, as for StD.
+    Written from that description: the sink is the first s = min(sink, topk)
+    positions of the span, the window the last topk - s.
+
+    Returns the absolute positions as an int64 array of length topk, sorted
+    ascending.
+    """
+    if not (0 <= topk <= vis_len) or sink < 0 or vis_start < 0:
+        raise ValueError("need 0 <= topk <= vis_len, sink >= 0, vis_start >= 0")
+    s = min(sink, topk)
+    sink_part = list(range(vis_start, vis_start + s))
+    vis_end = vis_start + vis_len
+    window_part = list(range(vis_end - (topk - s), vis_end))
+    return np.array(sorted(sink_part + window_part), dtype=np.int64)

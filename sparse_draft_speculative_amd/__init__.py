@@ -17,9 +17,12 @@ std_sparse_decode_attn_dlen / std_dense_verify_attn_dlen read the valid
 cache length from device memory, so a whole draft-verify cycle can be
 captured once and replayed; std_sparse_decode_attn_batch,
 std_dense_verify_attn_batch and std_accept_batch run the three decode steps
-for several independent sequences, one launch each.  std_check_idx
-counts index-list entries that break the draft call's preconditions (a
-debug aid).  std_hbm_read_probe
+for several independent sequences, one launch each (each sequence with its
+own valid length and, optionally, its own draft length).
+std_static_window_idx writes the index lists of the streaming-attention
+comparator (attention sink + recent window over the visual span) for the
+same draft calls.  std_check_idx counts index-list entries that break the
+draft call's preconditions (a debug aid).  std_hbm_read_probe
 is measurement harness: a plain streaming read that gives the attainable
 HBM bandwidth the HBM-bound kernels are compared with.
 
@@ -34,9 +37,10 @@ from ._lib import (  # noqa: F401
     std_sparse_decode_attn_batch, std_sparse_decode_batch_workspace,
     std_dense_verify_attn, std_dense_verify_workspace, std_dense_verify_attn_dlen,
     std_accept, std_accept_batch, std_dense_verify_attn_batch, std_dense_verify_batch_workspace,
-    std_check_idx, std_hbm_read_probe,
+    std_check_idx, std_hbm_read_probe, std_static_window_idx,
     std_prefill_text_attn, std_prefill_text_attn_workspace,
     PreparedCall, prepare_dense_verify, prepare_sparse_decode, prepare_select_topk,
     prepare_accept, prepare_dense_verify_dlen, prepare_sparse_decode_dlen,
-    prepare_prefill_text_attn,
+    prepare_prefill_text_attn, prepare_sparse_decode_batch, prepare_dense_verify_batch,
+    prepare_accept_batch,
 )

@@ -68,7 +68,7 @@ _SIGS = {
                                                 ctypes.POINTER(KV), Vis, _I]),
     "std_sparse_decode_attn_batch": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I,
                                                     ctypes.POINTER(KV), _P, _I, Vis, _P, _I, _P,
-                                                    _P, _SZ, _P]),
+                                                    _I, _P, _P, _SZ, _P]),
     "std_select_topk_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, Vis, _I,
                                         ctypes.POINTER(KV)]),
     "std_select_topk": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
@@ -79,7 +79,9 @@ _SIGS = {
                                                ctypes.POINTER(KV)]),
     "std_dense_verify_attn_batch": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
                                                    ctypes.POINTER(KV), _P, _I, _P, _P, _SZ, _P]),
-    "std_accept_batch": (ctypes.c_int, [_P, _I, _I, _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]),
+    "std_accept_batch": (ctypes.c_int, [_P, _I, _I, _P, _P, _I, ctypes.c_int, _P, _P, _P, _P,
+                                        _P]),
+    "std_static_window_idx": (ctypes.c_int, [_I, Vis, _I, _I, _P, _P]),
     "std_check_idx": (ctypes.c_int, [_P, _I, _I, Vis, _P, _P]),
     "std_prefill_text_attn_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I, _I]),
     "std_prefill_text_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I, _I,
@@ -133,6 +135,105 @@ def _dev(t, name):
     return t
 
 
+def _tensor(t, name, dtype=None, shape=None, min_numel=None):
+    """A contiguous tensor with the given dtype / exact shape / size.
+
+    Every wrapper and prepare_* helper validates its tensors here before a
+    pointer reaches the library (the C calls read and write exactly the
+    sizes implied by the shapes they are given); the device is checked
+    afterwards (_gpu), so a caller sees the specific mismatch first."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name} must be {' or '.join(str(a) for a in allowed)}, "
+                             f"got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, "
+                         f"got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+    return t
+
+
+def _gpu(**tensors):
+    """Every given (non-None) tensor lives on the GPU."""
+    for name, t in tensors.items():
+        if t is not None:
+            _dev(t, name)
+
+
+_KV_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _check_cache(k, v, dims, name="k"):
+    """k (and v, same shape and dtype): a [..][H_kv][capacity][d] cache of
+    ``dims`` dimensions in fp32 or bf16 with d 64 or 128 (the library
+    reports other head sizes as unsupported)."""
+    _tensor(k, name, _KV_DTYPES)
+    if k.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got {k.dim()}")
+    if v is not None:
+        _tensor(v, "v", k.dtype, k.shape)
+    return k.shape[-1]
+
+
+def _check_queries(q, k, dims, d, name="q"):
+    _tensor(q, name, k.dtype)
+    if q.dim() != dims or q.shape[-1] != d:
+        raise ValueError(f"{name} must have {dims} dimensions ending in head_dim {d}, "
+                         f"got {tuple(q.shape)}")
+    return q
+
+
+def _check_out(out, like, name="out"):
+    return _tensor(out, name, like.dtype, like.shape)
+
+
+def _check_len_dev(len_dev, n):
+    if len_dev is not None:
+        _tensor(len_dev, "len_dev", torch.int32, min_numel=n)
+        if n > 1 and len_dev.numel() != n:
+            raise ValueError(f"len_dev must hold {n} int32 lengths")
+        _gpu(len_dev=len_dev)
+
+
+def _check_gamma_dev(gamma_dev, n):
+    if gamma_dev is not None:
+        _tensor(gamma_dev, "gamma_dev", torch.int32, (n,))
+        _gpu(gamma_dev=gamma_dev)
+
+
+def _check_accept_io(draft, logits, gamma_rows, lead, out_tokens, n_out, margins, seq_len):
+    """draft [*lead][gamma]; logits [*lead][gamma+1][vocab]; outputs sized
+    for every sequence of the batch."""
+    _tensor(draft, "draft", torch.int32, (*lead, gamma_rows - 1))
+    _tensor(logits, "logits", _KV_DTYPES)
+    if logits.dim() != len(lead) + 2 or tuple(logits.shape[:-1]) != (*lead, gamma_rows):
+        raise ValueError(f"logits must be {(*lead, gamma_rows)} x vocab, got "
+                         f"{tuple(logits.shape)}")
+    nb = 1
+    for x in lead:
+        nb *= int(x)
+    if out_tokens is not None:
+        _tensor(out_tokens, "out_tokens", torch.int32, (*lead, gamma_rows))
+    if n_out is not None:
+        _tensor(n_out, "n_out", torch.int32, min_numel=nb)
+    if margins is not None:
+        _tensor(margins, "margins", torch.float32, (*lead, gamma_rows))
+    if seq_len is not None:
+        _tensor(seq_len, "seq_len", torch.int32, min_numel=nb)
+    _gpu(draft=draft, logits=logits, out_tokens=out_tokens, n_out=n_out, margins=margins,
+         seq_len=seq_len)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -162,6 +263,74 @@ def _workspace(nbytes, device, workspace):
     return workspace
 
 
+def _ws_bytes(ws):
+    return _nbytes(ws)
+
+
+# ----------------------------------------------------------------------------
+# Validated argument sets, shared by the wrappers and the prepare_* helpers.
+
+def _dense_args(q, k, v, out, batched=False):
+    """q [B?][n_q][H_q][d]; k, v [B?][H_kv][capacity][d]; out like q."""
+    lead = 1 if batched else 0
+    d = _check_cache(k, v, 3 + lead)
+    _check_queries(q, k, 3 + lead, d)
+    if batched and q.shape[0] != k.shape[0]:
+        raise ValueError(f"q and k must hold the same batch ({q.shape[0]} vs {k.shape[0]})")
+    if out is not None:
+        _check_out(out, q)
+    _gpu(q=q, k=k, v=v, out=out)
+    return d
+
+
+def _sparse_args(q, k, v, idx, out, batched=False):
+    """q [B?][H_q][d]; k, v [B?][H_kv][capacity][d]; idx [B?][H_kv][K] int32."""
+    lead = 1 if batched else 0
+    d = _check_cache(k, v, 3 + lead)
+    _check_queries(q, k, 2 + lead, d)
+    hkv = k.shape[lead]
+    _tensor(idx, "idx", torch.int32)
+    if idx.dim() != 2 + lead or idx.shape[lead] != hkv or (batched and idx.shape[0] != q.shape[0]):
+        want = "[B][H_kv][K]" if batched else "[H_kv][K]"
+        raise ValueError(f"idx must be {want} with H_kv = {hkv}, got {tuple(idx.shape)}")
+    if batched and k.shape[0] != q.shape[0]:
+        raise ValueError(f"q and k must hold the same batch ({q.shape[0]} vs {k.shape[0]})")
+    if out is not None:
+        _check_out(out, q)
+    _gpu(q=q, k=k, v=v, idx=idx, out=out)
+    return d
+
+
+def _select_args(q_text, k, idx_out, scores_out, lse, vis_len, topk):
+    d = _check_cache(k, None, 3)
+    _check_queries(q_text, k, 3, d, "q_text")
+    hq, n_text = q_text.shape[0], q_text.shape[1]
+    hkv = k.shape[0]
+    if idx_out is not None:
+        _tensor(idx_out, "idx_out", torch.int32, (hkv, topk))
+    if scores_out is not None:
+        _tensor(scores_out, "scores_out", torch.float32, (hkv, vis_len))
+    if lse is not None:
+        _tensor(lse, "lse", torch.float32)
+        if lse.numel() != hq * n_text:
+            raise ValueError(f"lse must hold H_q * n_text = {hq * n_text} float32 values")
+    _gpu(q_text=q_text, k=k, idx_out=idx_out, scores_out=scores_out, lse=lse)
+    return d
+
+
+def _prefill_args(q_text, k, v, out, lse_out):
+    d = _check_cache(k, v, 3)
+    _check_queries(q_text, k, 3, d, "q_text")
+    if out is not None:
+        _check_out(out, q_text)
+    if lse_out is not None:
+        _tensor(lse_out, "lse_out", torch.float32)
+        if lse_out.numel() != q_text.shape[0] * q_text.shape[1]:
+            raise ValueError("lse_out must be [H_q][n_text] float32")
+    _gpu(q_text=q_text, k=k, v=v, out=out, lse_out=lse_out)
+    return d
+
+
 # ----------------------------------------------------------------------------
 def std_dense_verify_workspace(shape, n_q, k, length):
     return load().std_dense_verify_workspace(ctypes.byref(shape), int(n_q),
@@ -171,18 +340,16 @@ def std_dense_verify_workspace(shape, n_q, k, length):
 def std_dense_verify_attn(q, k, v, length, out=None, scale=None, workspace=None, stream=None):
     """Dense verify attention.  q [n_q][H_q][d]; k, v [H_kv][capacity][d]."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
+    _dense_args(q, k, v, out)
     n_q, hq, d = q.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, length)
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out")
     ws = _workspace(lib.std_dense_verify_workspace(ctypes.byref(shape), n_q, ctypes.byref(kv)),
                     q.device, workspace)
     _check(lib.std_dense_verify_attn(ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv),
-                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+                                     _ptr(out), _ptr(ws), _ws_bytes(ws), _stream(stream)),
            "std_dense_verify_attn")
     return out
 
@@ -198,28 +365,21 @@ def std_dense_verify_attn_batch(q, k, v, max_len, len_dev=None, len_offset=0, ou
                                 scale=None, workspace=None, stream=None):
     """Dense verify for B sequences in one launch.  q [B][n_q][H_q][d];
     k, v [B][H_kv][capacity][d]; len_dev None (every sequence has length
-    max_len) or [B] int32 device lengths: min(max(len_dev[b] + len_offset, 1),
+    max_len) or [B] int32 device lengths: min(max(len_dev[b] + len_offset, n_q),
     max_len)."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
+    _check_len_dev(len_dev, q.shape[0])
+    _dense_args(q, k, v, out, batched=True)
     B, n_q, hq, d = q.shape
-    if k.dim() != 4 or k.shape[0] != B or v.shape != k.shape:
-        raise ValueError("k and v must be [B][H_kv][capacity][d] with the batch of q")
-    if len_dev is not None:
-        _dev(len_dev, "len_dev")
-        if len_dev.dtype != torch.int32 or len_dev.numel() != B:
-            raise ValueError("len_dev must be [B] int32")
     shape = attn_shape(hq, k.shape[1], d, scale)
     kv = KV(k.data_ptr(), v.data_ptr(), k.shape[2], int(max_len), _dtype_code(k))
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out")
     ws = _workspace(std_dense_verify_batch_workspace(shape, n_q, B, k, max_len), q.device,
                     workspace)
     _check(lib.std_dense_verify_attn_batch(ctypes.byref(shape), _ptr(q), n_q, B, ctypes.byref(kv),
                                            _ptr(len_dev), int(len_offset), _ptr(out), _ptr(ws),
-                                           ws.numel(), _stream(stream)),
+                                           _ws_bytes(ws), _stream(stream)),
            "std_dense_verify_attn_batch")
     return out
 
@@ -227,23 +387,20 @@ def std_dense_verify_attn_batch(q, k, v, max_len, len_dev=None, len_offset=0, ou
 def std_dense_verify_attn_dlen(q, k, v, max_len, len_dev, len_offset, out=None, scale=None,
                                workspace=None, stream=None):
     """Dense verify with the valid length read on the device:
-    min(max(len_dev[0] + len_offset, 1), max_len)."""
+    min(max(len_dev[0] + len_offset, n_q), max_len)."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (len_dev, "len_dev")):
-        _dev(t, n)
-    if len_dev.dtype != torch.int32:
-        raise ValueError("len_dev must be int32")
+    _check_len_dev(len_dev, 1)
+    _dense_args(q, k, v, out)
     n_q, hq, d = q.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, max_len)
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out")
     ws = _workspace(lib.std_dense_verify_workspace(ctypes.byref(shape), n_q, ctypes.byref(kv)),
                     q.device, workspace)
     _check(lib.std_dense_verify_attn_dlen(ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv),
                                           _ptr(len_dev), int(len_offset), _ptr(out), _ptr(ws),
-                                          ws.numel(), _stream(stream)),
+                                          _ws_bytes(ws), _stream(stream)),
            "std_dense_verify_attn_dlen")
     return out
 
@@ -258,25 +415,19 @@ def std_sparse_decode_attn(q, k, v, length, vis_start, vis_len, idx, out=None, s
                            workspace=None, stream=None):
     """Sparse draft attention.  q [H_q][d]; idx [H_kv][K] int32 (K may be 0)."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx")):
-        _dev(t, n)
-    if idx.dtype != torch.int32:
-        raise ValueError("idx must be int32")
+    _sparse_args(q, k, v, idx, out)
     hq, d = q.shape
     hkv = k.shape[0]
-    topk = idx.shape[1] if idx.dim() == 2 else 0
-    if idx.dim() != 2 or idx.shape[0] != hkv:
-        raise ValueError("idx must be [H_kv][K]")
+    topk = idx.shape[1]
     shape = attn_shape(hq, hkv, d, scale)
     kv = kv_desc(k, v, length)
     vis = Vis(vis_start, vis_len)
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out")
     ws = _workspace(lib.std_sparse_decode_workspace(ctypes.byref(shape), ctypes.byref(kv), vis,
                                                     topk), q.device, workspace)
     _check(lib.std_sparse_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(kv), vis,
-                                      _ptr(idx), topk, _ptr(out), _ptr(ws), ws.numel(),
+                                      _ptr(idx), topk, _ptr(out), _ptr(ws), _ws_bytes(ws),
                                       _stream(stream)),
            "std_sparse_decode_attn")
     return out
@@ -285,28 +436,24 @@ def std_sparse_decode_attn(q, k, v, length, vis_start, vis_len, idx, out=None, s
 def std_sparse_decode_attn_dlen(q, k, v, max_len, len_dev, len_offset, vis_start, vis_len, idx,
                                 out=None, scale=None, workspace=None, stream=None):
     """Sparse draft attention with the valid length read on the device:
-    min(max(len_dev[0] + len_offset, 1), max_len)."""
+    min(max(len_dev[0] + len_offset, lo), max_len), lo = vis_start + vis_len
+    (+1 with neither a prefix nor a selected position)."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (len_dev, "len_dev")):
-        _dev(t, n)
-    if idx.dtype != torch.int32 or len_dev.dtype != torch.int32:
-        raise ValueError("idx and len_dev must be int32")
+    _check_len_dev(len_dev, 1)
+    _sparse_args(q, k, v, idx, out)
     hq, d = q.shape
     hkv = k.shape[0]
-    if idx.dim() != 2 or idx.shape[0] != hkv:
-        raise ValueError("idx must be [H_kv][K]")
     topk = idx.shape[1]
     shape = attn_shape(hq, hkv, d, scale)
     kv = kv_desc(k, v, max_len)
     vis = Vis(vis_start, vis_len)
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out")
     ws = _workspace(lib.std_sparse_decode_workspace(ctypes.byref(shape), ctypes.byref(kv), vis,
                                                     topk), q.device, workspace)
     _check(lib.std_sparse_decode_attn_dlen(ctypes.byref(shape), _ptr(q), ctypes.byref(kv),
                                            _ptr(len_dev), int(len_offset), vis, _ptr(idx), topk,
-                                           _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+                                           _ptr(out), _ptr(ws), _ws_bytes(ws), _stream(stream)),
            "std_sparse_decode_attn_dlen")
     return out
 
@@ -320,41 +467,37 @@ def std_sparse_decode_batch_workspace(shape, batch, k, length, vis_start, vis_le
 
 
 def std_sparse_decode_attn_batch(q, k, v, max_len, vis_start, vis_len, idx, len_dev=None,
-                                 len_offset=0, out=None, scale=None, workspace=None, stream=None):
+                                 len_offset=0, gamma_dev=None, step=0, out=None, scale=None,
+                                 workspace=None, stream=None):
     """Sparse draft attention for B sequences in one launch.
 
     q [B][H_q][d]; k, v [B][H_kv][capacity][d]; idx [B][H_kv][K] int32;
     len_dev None (every sequence has length max_len) or [B] int32 device
-    lengths, sequence b using min(max(len_dev[b] + len_offset, 1), max_len).
+    lengths, sequence b using min(max(len_dev[b] + len_offset, lo), max_len).
+    gamma_dev None or [B] int32 device draft lengths: the call is draft step
+    ``step`` and sequence b takes part only while step < gamma_dev[b] (the
+    others' rows of ``out`` are left as they were).
     """
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx")):
-        _dev(t, n)
-    if idx.dtype != torch.int32:
-        raise ValueError("idx must be int32")
+    B = q.shape[0]
+    _check_len_dev(len_dev, B)
+    _check_gamma_dev(gamma_dev, B)
+    _sparse_args(q, k, v, idx, out, batched=True)
     B, hq, d = q.shape
-    if k.dim() != 4 or k.shape[0] != B or v.shape != k.shape:
-        raise ValueError("k and v must be [B][H_kv][capacity][d] with the batch of q")
     hkv, cap = k.shape[1], k.shape[2]
-    if idx.dim() != 3 or idx.shape[0] != B or idx.shape[1] != hkv:
-        raise ValueError("idx must be [B][H_kv][K]")
-    if len_dev is not None:
-        _dev(len_dev, "len_dev")
-        if len_dev.dtype != torch.int32 or len_dev.numel() != B:
-            raise ValueError("len_dev must be [B] int32")
     topk = idx.shape[2]
     shape = attn_shape(hq, hkv, d, scale)
     kv = KV(k.data_ptr(), v.data_ptr(), cap, int(max_len), _dtype_code(k))
     vis = Vis(vis_start, vis_len)
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out")
     ws = _workspace(lib.std_sparse_decode_batch_workspace(ctypes.byref(shape), B,
                                                           ctypes.byref(kv), vis, topk),
                     q.device, workspace)
     _check(lib.std_sparse_decode_attn_batch(ctypes.byref(shape), _ptr(q), B, ctypes.byref(kv),
                                             _ptr(len_dev), int(len_offset), vis, _ptr(idx), topk,
-                                            _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+                                            _ptr(gamma_dev), int(step), _ptr(out), _ptr(ws),
+                                            _ws_bytes(ws), _stream(stream)),
            "std_sparse_decode_attn_batch")
     return out
 
@@ -373,8 +516,7 @@ def std_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, lse
     Returns idx [H_kv][topk] int32 (and the fp32 scores if want_scores).
     """
     lib = load()
-    _dev(q_text, "q_text")
-    _dev(k, "k")
+    _select_args(q_text, k, idx_out, scores_out, lse, vis_len, topk)
     hq, n_text, d = q_text.shape
     hkv = k.shape[0]
     shape = attn_shape(hq, hkv, d, scale)
@@ -384,13 +526,11 @@ def std_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, lse
         idx_out = torch.empty(hkv, topk, dtype=torch.int32, device=k.device)
     if scores_out is None and want_scores:
         scores_out = torch.empty(hkv, vis_len, dtype=torch.float32, device=k.device)
-    if lse is not None:
-        _dev(lse, "lse")
     ws = _workspace(lib.std_select_topk_workspace(ctypes.byref(shape), n_text, vis, topk,
                                                   ctypes.byref(kv)), k.device, workspace)
     _check(lib.std_select_topk(ctypes.byref(shape), _ptr(q_text), text_start, n_text,
                                ctypes.byref(kv), vis, topk, _ptr(lse), _ptr(idx_out),
-                               _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)),
+                               _ptr(scores_out), _ptr(ws), _ws_bytes(ws), _stream(stream)),
            "std_select_topk")
     return (idx_out, scores_out) if want_scores else idx_out
 
@@ -402,9 +542,11 @@ def std_accept(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len
     Returns (out_tokens [gamma+1] int32, n_out [1] int32) on the device.
     """
     lib = load()
-    _dev(draft, "draft")
-    _dev(logits, "logits")
+    _tensor(draft, "draft", torch.int32)
+    if draft.dim() != 1:
+        raise ValueError("draft must be [gamma] int32")
     gamma = draft.numel()
+    _check_accept_io(draft, logits, gamma + 1, (), out_tokens, n_out, margins, seq_len)
     vocab = logits.shape[1]
     dev = logits.device
     if out_tokens is None:
@@ -415,6 +557,32 @@ def std_accept(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len
                           _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len),
                           _stream(stream)),
            "std_accept")
+    return out_tokens, n_out
+
+
+def std_accept_batch(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len=None,
+                     gamma_dev=None, stream=None):
+    """Greedy acceptance for B sequences.  draft [B][gamma] int32; logits
+    [B][gamma+1][vocab].  gamma_dev None or [B] int32 device draft lengths
+    (each clamped into [0, gamma]; gamma is then the row stride).  Returns
+    (out_tokens [B][gamma+1], n_out [B])."""
+    lib = load()
+    _tensor(draft, "draft", torch.int32)
+    if draft.dim() != 2:
+        raise ValueError("draft must be [B][gamma] int32")
+    B, gamma = draft.shape
+    _check_gamma_dev(gamma_dev, B)
+    _check_accept_io(draft, logits, gamma + 1, (B,), out_tokens, n_out, margins, seq_len)
+    vocab = logits.shape[2]
+    dev = logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty(B, gamma + 1, dtype=torch.int32, device=dev)
+    if n_out is None:
+        n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib.std_accept_batch(_ptr(draft), gamma, B, _ptr(gamma_dev), _ptr(logits), vocab,
+                                _dtype_code(logits), _ptr(out_tokens), _ptr(n_out),
+                                _ptr(margins), _ptr(seq_len), _stream(stream)),
+           "std_accept_batch")
     return out_tokens, n_out
 
 
@@ -430,29 +598,37 @@ def std_prefill_text_attn(q_text, k, v, length, text_start, out=None, lse_out=No
     k, v [H_kv][capacity][d] (valid length ``length``).  Returns
     (out [H_q][n_text][d] bf16, lse [H_q][n_text] fp32 natural log or None)."""
     lib = load()
-    for t, n in ((q_text, "q_text"), (k, "k"), (v, "v")):
-        _dev(t, n)
-    if q_text.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
-        raise ValueError("q_text [H_q][n_text][d]; k, v [H_kv][capacity][d]")
+    _prefill_args(q_text, k, v, out, lse_out)
     hq, n_text, d = q_text.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, length)
     if out is None:
         out = torch.empty_like(q_text)
-    _dev(out, "out")
     if lse_out is None and want_lse:
         lse_out = torch.empty(hq, n_text, dtype=torch.float32, device=q_text.device)
-    if lse_out is not None:
-        _dev(lse_out, "lse_out")
-        if lse_out.dtype != torch.float32 or lse_out.numel() != hq * n_text:
-            raise ValueError("lse_out must be [H_q][n_text] float32")
     ws = _workspace(lib.std_prefill_text_attn_workspace(ctypes.byref(shape), text_start, n_text),
                     q_text.device, workspace)
     _check(lib.std_prefill_text_attn(ctypes.byref(shape), _ptr(q_text), int(text_start),
                                      int(n_text), ctypes.byref(kv), _ptr(out), _ptr(lse_out),
-                                     _ptr(ws), ws.numel(), _stream(stream)),
+                                     _ptr(ws), _ws_bytes(ws), _stream(stream)),
            "std_prefill_text_attn")
     return out, lse_out
+
+
+def std_static_window_idx(n_kv_heads, vis_start, vis_len, sink, topk, idx_out=None,
+                          device="cuda", stream=None):
+    """Index lists of the streaming-attention comparator: for each of the
+    n_kv_heads heads the first min(sink, topk) visual positions and the last
+    topk - min(sink, topk), ascending.  Returns idx [H_kv][topk] int32."""
+    lib = load()
+    if idx_out is None:
+        idx_out = torch.empty(int(n_kv_heads), int(topk), dtype=torch.int32, device=device)
+    _tensor(idx_out, "idx_out", torch.int32, (n_kv_heads, topk))
+    _gpu(idx_out=idx_out)
+    _check(lib.std_static_window_idx(int(n_kv_heads), Vis(vis_start, vis_len), int(sink),
+                                     int(topk), _ptr(idx_out), _stream(stream)),
+           "std_static_window_idx")
+    return idx_out
 
 
 def std_check_idx(idx, vis_start, vis_len, bad_out=None, stream=None):
@@ -460,12 +636,13 @@ def std_check_idx(idx, vis_start, vis_len, bad_out=None, stream=None):
     span or not above the previous entry of their head.  Returns the count
     as a [1] int32 device tensor (0: the list meets every precondition)."""
     lib = load()
-    _dev(idx, "idx")
-    if idx.dtype != torch.int32 or idx.dim() != 2:
+    _tensor(idx, "idx", torch.int32)
+    if idx.dim() != 2:
         raise ValueError("idx must be [H_kv][K] int32")
     if bad_out is None:
         bad_out = torch.empty(1, dtype=torch.int32, device=idx.device)
-    _dev(bad_out, "bad_out")
+    _tensor(bad_out, "bad_out", torch.int32, min_numel=1)
+    _gpu(idx=idx, bad_out=bad_out)
     _check(lib.std_check_idx(_ptr(idx), idx.shape[0], idx.shape[1], Vis(vis_start, vis_len),
                              _ptr(bad_out), _stream(stream)),
            "std_check_idx")
@@ -481,35 +658,11 @@ def std_hbm_read_probe(buf, sink=None, stream=None):
     if sink is None:
         sink = torch.empty(PROBE_SINK_WORDS, dtype=torch.int32, device=buf.device)
     _dev(sink, "sink")
-    if sink.numel() * sink.element_size() < 4 * PROBE_SINK_WORDS:
+    if _nbytes(sink) < 4 * PROBE_SINK_WORDS:
         raise ValueError(f"sink must hold {PROBE_SINK_WORDS} 32-bit words")
-    _check(lib.std_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
-                                  _stream(stream)),
+    _check(lib.std_hbm_read_probe(_ptr(buf), _nbytes(buf), _ptr(sink), _stream(stream)),
            "std_hbm_read_probe")
     return sink
-
-
-def std_accept_batch(draft, logits, out_tokens=None, n_out=None, margins=None, seq_len=None,
-                     stream=None):
-    """Greedy acceptance for B sequences.  draft [B][gamma] int32; logits
-    [B][gamma+1][vocab].  Returns (out_tokens [B][gamma+1], n_out [B])."""
-    lib = load()
-    _dev(draft, "draft")
-    _dev(logits, "logits")
-    B, gamma = draft.shape
-    vocab = logits.shape[2]
-    if logits.shape[:2] != (B, gamma + 1):
-        raise ValueError("logits must be [B][gamma+1][vocab]")
-    dev = logits.device
-    if out_tokens is None:
-        out_tokens = torch.empty(B, gamma + 1, dtype=torch.int32, device=dev)
-    if n_out is None:
-        n_out = torch.empty(B, dtype=torch.int32, device=dev)
-    _check(lib.std_accept_batch(_ptr(draft), gamma, B, _ptr(logits), vocab, _dtype_code(logits),
-                                _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len),
-                                _stream(stream)),
-           "std_accept_batch")
-    return out_tokens, n_out
 
 
 # ----------------------------------------------------------------------------
@@ -534,26 +687,25 @@ class PreparedCall:
 
 
 def prepare_dense_verify(q, k, v, out, workspace, stream=None, scale=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (workspace, "workspace")):
-        _dev(t, n)
+    _dense_args(q, k, v, out)
+    _dev(workspace, "workspace")
     n_q, hq, d = q.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, k.shape[1])
     args = (ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv), _ptr(out), _ptr(workspace),
-            workspace.numel(), _stream(stream))
+            _nbytes(workspace), _stream(stream))
     return PreparedCall("std_dense_verify_attn", args, kv, (shape, kv, q, k, v, out, workspace))
 
 
 def prepare_sparse_decode(q, k, v, vis_start, vis_len, idx, out, workspace, stream=None,
                           scale=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (out, "out"),
-                 (workspace, "workspace")):
-        _dev(t, n)
+    _sparse_args(q, k, v, idx, out)
+    _dev(workspace, "workspace")
     hq, d = q.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, k.shape[1])
     args = (ctypes.byref(shape), _ptr(q), ctypes.byref(kv), Vis(vis_start, vis_len), _ptr(idx),
-            idx.shape[1], _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+            idx.shape[1], _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream))
     return PreparedCall("std_sparse_decode_attn", args, kv,
                         (shape, kv, q, k, v, idx, out, workspace))
 
@@ -562,14 +714,14 @@ def prepare_dense_verify_dlen(q, k, v, out, workspace, len_dev, len_offset, max_
                               stream=None, scale=None):
     """Prepared dense verify reading its length from len_dev (see
     std_dense_verify_attn_dlen); max_len defaults to the cache capacity."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (workspace, "workspace"),
-                 (len_dev, "len_dev")):
-        _dev(t, n)
+    _dense_args(q, k, v, out)
+    _dev(workspace, "workspace")
+    _check_len_dev(len_dev, 1)
     n_q, hq, d = q.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, k.shape[1] if max_len is None else max_len)
     args = (ctypes.byref(shape), _ptr(q), n_q, ctypes.byref(kv), _ptr(len_dev), int(len_offset),
-            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+            _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream))
     return PreparedCall("std_dense_verify_attn_dlen", args, kv,
                         (shape, kv, q, k, v, out, workspace, len_dev))
 
@@ -577,52 +729,103 @@ def prepare_dense_verify_dlen(q, k, v, out, workspace, len_dev, len_offset, max_
 def prepare_sparse_decode_dlen(q, k, v, vis_start, vis_len, idx, out, workspace, len_dev,
                                len_offset, max_len=None, stream=None, scale=None):
     """Prepared sparse draft attention reading its length from len_dev."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (out, "out"),
-                 (workspace, "workspace"), (len_dev, "len_dev")):
-        _dev(t, n)
+    _sparse_args(q, k, v, idx, out)
+    _dev(workspace, "workspace")
+    _check_len_dev(len_dev, 1)
     hq, d = q.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, k.shape[1] if max_len is None else max_len)
     args = (ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(len_dev), int(len_offset),
             Vis(vis_start, vis_len), _ptr(idx), idx.shape[1], _ptr(out), _ptr(workspace),
-            workspace.numel(), _stream(stream))
+            _nbytes(workspace), _stream(stream))
     return PreparedCall("std_sparse_decode_attn_dlen", args, kv,
                         (shape, kv, q, k, v, idx, out, workspace, len_dev))
 
 
+def prepare_sparse_decode_batch(q, k, v, max_len, vis_start, vis_len, idx, out, workspace,
+                                len_dev=None, len_offset=0, gamma_dev=None, step=0, stream=None,
+                                scale=None):
+    """Prepared batched sparse draft attention (see std_sparse_decode_attn_batch)."""
+    B = q.shape[0]
+    _check_len_dev(len_dev, B)
+    _check_gamma_dev(gamma_dev, B)
+    _sparse_args(q, k, v, idx, out, batched=True)
+    _dev(workspace, "workspace")
+    B, hq, d = q.shape
+    shape = attn_shape(hq, k.shape[1], d, scale)
+    kv = KV(k.data_ptr(), v.data_ptr(), k.shape[2], int(max_len), _dtype_code(k))
+    args = (ctypes.byref(shape), _ptr(q), B, ctypes.byref(kv), _ptr(len_dev), int(len_offset),
+            Vis(vis_start, vis_len), _ptr(idx), idx.shape[2], _ptr(gamma_dev), int(step),
+            _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    return PreparedCall("std_sparse_decode_attn_batch", args, kv,
+                        (shape, kv, q, k, v, idx, out, workspace, len_dev, gamma_dev))
+
+
+def prepare_dense_verify_batch(q, k, v, max_len, out, workspace, len_dev=None, len_offset=0,
+                               stream=None, scale=None):
+    """Prepared batched dense verify (see std_dense_verify_attn_batch)."""
+    _check_len_dev(len_dev, q.shape[0])
+    _dense_args(q, k, v, out, batched=True)
+    _dev(workspace, "workspace")
+    B, n_q, hq, d = q.shape
+    shape = attn_shape(hq, k.shape[1], d, scale)
+    kv = KV(k.data_ptr(), v.data_ptr(), k.shape[2], int(max_len), _dtype_code(k))
+    args = (ctypes.byref(shape), _ptr(q), n_q, B, ctypes.byref(kv), _ptr(len_dev),
+            int(len_offset), _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    return PreparedCall("std_dense_verify_attn_batch", args, kv,
+                        (shape, kv, q, k, v, out, workspace, len_dev))
+
+
 def prepare_prefill_text_attn(q_text, k, v, length, text_start, out, lse_out, workspace,
                               stream=None, scale=None):
-    for t, n in ((q_text, "q_text"), (k, "k"), (v, "v"), (out, "out"), (lse_out, "lse_out"),
-                 (workspace, "workspace")):
-        _dev(t, n)
+    _prefill_args(q_text, k, v, out, lse_out)
+    _dev(workspace, "workspace")
     hq, n_text, d = q_text.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, v, length)
     args = (ctypes.byref(shape), _ptr(q_text), int(text_start), n_text, ctypes.byref(kv),
-            _ptr(out), _ptr(lse_out), _ptr(workspace), workspace.numel(), _stream(stream))
+            _ptr(out), _ptr(lse_out), _ptr(workspace), _nbytes(workspace), _stream(stream))
     return PreparedCall("std_prefill_text_attn", args, kv,
                         (shape, kv, q_text, k, v, out, lse_out, workspace))
 
 
 def prepare_select_topk(q_text, k, length, text_start, vis_start, vis_len, topk, idx_out,
                         workspace, scores_out=None, lse=None, stream=None, scale=None):
-    for t, n in ((q_text, "q_text"), (k, "k"), (idx_out, "idx_out"), (workspace, "workspace")):
-        _dev(t, n)
+    _select_args(q_text, k, idx_out, scores_out, lse, vis_len, topk)
+    _dev(workspace, "workspace")
     hq, n_text, d = q_text.shape
     shape = attn_shape(hq, k.shape[0], d, scale)
     kv = kv_desc(k, k, length)
     args = (ctypes.byref(shape), _ptr(q_text), text_start, n_text, ctypes.byref(kv),
             Vis(vis_start, vis_len), topk, _ptr(lse), _ptr(idx_out), _ptr(scores_out),
-            _ptr(workspace), workspace.numel(), _stream(stream))
+            _ptr(workspace), _nbytes(workspace), _stream(stream))
     return PreparedCall("std_select_topk", args, kv,
                         (shape, kv, q_text, k, idx_out, workspace, scores_out, lse))
 
 
 def prepare_accept(draft, logits, out_tokens, n_out, margins=None, seq_len=None, stream=None):
-    for t, n in ((draft, "draft"), (logits, "logits"), (out_tokens, "out_tokens"),
-                 (n_out, "n_out")):
-        _dev(t, n)
-    args = (_ptr(draft), draft.numel(), _ptr(logits), logits.shape[1], _dtype_code(logits),
+    _tensor(draft, "draft", torch.int32)
+    if draft.dim() != 1:
+        raise ValueError("draft must be [gamma] int32")
+    gamma = draft.numel()
+    _check_accept_io(draft, logits, gamma + 1, (), out_tokens, n_out, margins, seq_len)
+    args = (_ptr(draft), gamma, _ptr(logits), logits.shape[1], _dtype_code(logits),
             _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len), _stream(stream))
     return PreparedCall("std_accept", args, None,
                         (draft, logits, out_tokens, n_out, margins, seq_len))
+
+
+def prepare_accept_batch(draft, logits, out_tokens, n_out, margins=None, seq_len=None,
+                         gamma_dev=None, stream=None):
+    """Prepared batched acceptance (see std_accept_batch)."""
+    _tensor(draft, "draft", torch.int32)
+    if draft.dim() != 2:
+        raise ValueError("draft must be [B][gamma] int32")
+    B, gamma = draft.shape
+    _check_gamma_dev(gamma_dev, B)
+    _check_accept_io(draft, logits, gamma + 1, (B,), out_tokens, n_out, margins, seq_len)
+    args = (_ptr(draft), gamma, B, _ptr(gamma_dev), _ptr(logits), logits.shape[2],
+            _dtype_code(logits), _ptr(out_tokens), _ptr(n_out), _ptr(margins), _ptr(seq_len),
+            _stream(stream))
+    return PreparedCall("std_accept_batch", args, None,
+                        (draft, logits, out_tokens, n_out, margins, seq_len, gamma_dev))

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstdspec.so")
-SOURCES = ["api.hip", "attention.hip", "select.hip", "accept.hip", "probe.hip", "check.hip", "prefill.hip"]
+SOURCES = ["api.hip", "attention.hip", "select.hip", "accept.hip", "probe.hip", "check.hip",
+           "prefill.hip", "window.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

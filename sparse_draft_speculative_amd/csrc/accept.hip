@@ -8,8 +8,11 @@
 //  argmax_rows  -- one 1024-thread workgroup per logit row: argmax (ties to
 //                  the lowest id) and margin = top1 - top2.  The prediction
 //                  is written straight into out_tokens[row].
-//  accept_commit -- one wave: n = length of the agreeing prefix, n_out = n+1,
-//                  slots after the bonus set to -1, optional seq_len += n+1.
+//  accept_commit -- one wave per sequence: n = length of the agreeing
+//                  prefix, n_out = n+1, slots after the bonus set to -1,
+//                  optional seq_len += n+1.
+// A batch may give each sequence its own draft length gamma_b <= gamma (the
+// row stride): rows past gamma_b + 1 are not read.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -33,6 +36,11 @@ __device__ __forceinline__ Best merge(Best a, Best b) {
 
 constexpr int kArgmaxThreads = 1024;
 
+// Draft length of sequence b: gamma_dev[b] clamped into [0, gamma], or gamma.
+__device__ __forceinline__ int seq_gamma(const int32_t* gamma_dev, int b, int gamma) {
+  return gamma_dev ? min(max(gamma_dev[b], 0), gamma) : gamma;
+}
+
 __device__ __forceinline__ void consider(Best& b, float x, int j) {
   // elements reach a thread in increasing id order: the first maximum wins
   if (x > b.v || b.i == 0x7fffffff) { b.v2 = fmaxf(b.v2, b.v); b.v = x; b.i = j; }
@@ -43,11 +51,20 @@ __device__ __forceinline__ void consider(Best& b, float x, int j) {
 // with 16-byte loads (8 ids per thread per step), others element by element.
 template <typename T>
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T* __restrict__ logits,
-                                                              int vocab,
+                                                              int vocab, int gamma,
+                                                              const int32_t* __restrict__ gamma_dev,
                                                               int32_t* __restrict__ pred,
                                                               float* __restrict__ margins) {
   __shared__ Best sh[kArgmaxThreads / kWave];
   const int row = blockIdx.x, tid = threadIdx.x;
+  // row i of sequence b; rows past the sequence's own gamma_b + 1 are unused
+  if (gamma_dev && row % (gamma + 1) > seq_gamma(gamma_dev, row / (gamma + 1), gamma)) {
+    if (tid == 0) {
+      pred[row] = -1;
+      if (margins) margins[row] = __builtin_nanf("");
+    }
+    return;
+  }
   const T* lr = logits + (size_t)row * vocab;
   Best b{-INFINITY, 0x7fffffff, -INFINITY};
   constexpr int kVec = 16 / sizeof(T);                 // ids per 16-byte load
@@ -89,6 +106,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T* __restric
 }
 
 __global__ __launch_bounds__(64) void accept_commit(const int32_t* __restrict__ draft, int gamma,
+                                                    const int32_t* __restrict__ gamma_dev,
                                                     int32_t* __restrict__ out_tokens,
                                                     int32_t* __restrict__ n_out,
                                                     int32_t* __restrict__ seq_len) {
@@ -100,12 +118,13 @@ __global__ __launch_bounds__(64) void accept_commit(const int32_t* __restrict__ 
   if (seq_len) seq_len += b;
   __shared__ int sh_n;
   const int lane = threadIdx.x;
-  if (lane == 0) sh_n = gamma;
+  const int gb = seq_gamma(gamma_dev, b, gamma);     // this sequence's drafts
+  if (lane == 0) sh_n = gb;
   __syncthreads();
   // first j with draft[j] != pred[j] (pred lives in out_tokens)
-  for (int base = 0; base < gamma; base += 64) {
+  for (int base = 0; base < gb; base += 64) {
     const int j = base + lane;
-    const bool miss = j < gamma && draft[j] != out_tokens[j];
+    const bool miss = j < gb && draft[j] != out_tokens[j];
     const unsigned long long mask = __ballot(miss);
     if (mask) {
       if (lane == 0) sh_n = base + __ffsll((long long)mask) - 1;
@@ -123,21 +142,21 @@ __global__ __launch_bounds__(64) void accept_commit(const int32_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const void* logits,
-                         int vocab, bool bf16, int32_t* out_tokens, int32_t* n_out, float* margins,
-                         int32_t* seq_len, hipStream_t st) {
+hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const int32_t* gamma_dev,
+                         const void* logits, int vocab, bool bf16, int32_t* out_tokens,
+                         int32_t* n_out, float* margins, int32_t* seq_len, hipStream_t st) {
   // one argmax workgroup per logit row of every sequence ([batch][gamma+1]
   // rows back to back), then one commit wave per sequence
   const int rows = batch * (gamma + 1);
   if (bf16)
     argmax_rows<uint16_t><<<rows, kArgmaxThreads, 0, st>>>(
-        static_cast<const uint16_t*>(logits), vocab, out_tokens, margins);
+        static_cast<const uint16_t*>(logits), vocab, gamma, gamma_dev, out_tokens, margins);
   else
     argmax_rows<float><<<rows, kArgmaxThreads, 0, st>>>(static_cast<const float*>(logits), vocab,
-                                                       out_tokens, margins);
+                                                       gamma, gamma_dev, out_tokens, margins);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  accept_commit<<<batch, 64, 0, st>>>(draft, gamma, out_tokens, n_out, seq_len);
+  accept_commit<<<batch, 64, 0, st>>>(draft, gamma, gamma_dev, out_tokens, n_out, seq_len);
   return hipGetLastError();
 }
 

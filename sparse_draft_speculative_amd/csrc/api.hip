@@ -219,6 +219,7 @@ std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q,
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
   a.capacity = kv->capacity; a.len = kv->len; a.n_q = n_q; a.batch = batch;
   a.len_dev = len_dev; a.len_off = len_off;
+  a.len_lo = n_q;                         // every query row sees a key
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = false;
   a.ml = static_cast<float*>(ws);
@@ -273,9 +274,11 @@ namespace {
 
 std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t batch,
                            const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
-                           std_vis_t vis, const int32_t* idx, int32_t topk, void* out, void* ws,
+                           std_vis_t vis, const int32_t* idx, int32_t topk,
+                           const int32_t* gamma_dev, int32_t step, void* out, void* ws,
                            size_t ws_bytes, void* stream) {
   TRY(check_sparse_call(s, kv, vis, topk, batch));
+  CHECK(!gamma_dev || step >= 0, STD_ERR_INVALID_ARGUMENT, "need step (%d) >= 0", step);
   TRY(check_kv(kv, true));
   CHECK(q && out, STD_ERR_INVALID_ARGUMENT, "q / out is null");
   CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
@@ -289,6 +292,10 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t bat
   a.hq = s->n_q_heads; a.hkv = s->n_kv_heads; a.d = s->head_dim; a.scale = s->scale;
   a.capacity = kv->capacity; a.len = kv->len; a.n_q = 1; a.batch = batch;
   a.len_dev = len_dev; a.len_off = len_off;
+  // the query sits after the visual span; with neither a prefix nor a
+  // selected position the key list needs one position past it
+  a.len_lo = vis.vis_start + vis.vis_len + (vis.vis_start + topk == 0 ? 1 : 0);
+  a.gamma_dev = gamma_dev; a.step = step;
   a.bf16 = kv->dtype == STD_DTYPE_BF16;
   a.sparse = true; a.idx = idx;
   a.vis_start = vis.vis_start; a.vis_len = vis.vis_len; a.topk = topk;
@@ -305,7 +312,8 @@ extern "C" {
 std_status_t std_sparse_decode_attn(const std_attn_shape_t* s, const void* q, const std_kv_t* kv,
                                     std_vis_t vis, const int32_t* idx, int32_t topk, void* out,
                                     void* ws, size_t ws_bytes, void* stream) {
-  return sparse_decode(s, q, 1, kv, nullptr, 0, vis, idx, topk, out, ws, ws_bytes, stream);
+  return sparse_decode(s, q, 1, kv, nullptr, 0, vis, idx, topk, nullptr, 0, out, ws, ws_bytes,
+                       stream);
 }
 
 std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* q,
@@ -314,8 +322,8 @@ std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* 
                                          int32_t topk, void* out, void* ws, size_t ws_bytes,
                                          void* stream) {
   CHECK(len_dev, STD_ERR_INVALID_ARGUMENT, "len_dev is null");
-  return sparse_decode(s, q, 1, kv, len_dev, len_offset, vis, idx, topk, out, ws, ws_bytes,
-                       stream);
+  return sparse_decode(s, q, 1, kv, len_dev, len_offset, vis, idx, topk, nullptr, 0, out, ws,
+                       ws_bytes, stream);
 }
 
 size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* s, int32_t batch,
@@ -329,9 +337,10 @@ std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* s, const void*
                                           int32_t batch, const std_kv_t* kv,
                                           const int32_t* len_dev, int32_t len_offset,
                                           std_vis_t vis, const int32_t* idx, int32_t topk,
+                                          const int32_t* gamma_dev_or_null, int32_t step,
                                           void* out, void* ws, size_t ws_bytes, void* stream) {
-  return sparse_decode(s, q, batch, kv, len_dev, len_offset, vis, idx, topk, out, ws, ws_bytes,
-                       stream);
+  return sparse_decode(s, q, batch, kv, len_dev, len_offset, vis, idx, topk, gamma_dev_or_null,
+                       step, out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- selection
@@ -398,14 +407,15 @@ std_status_t std_select_topk(const std_attn_shape_t* s, const void* q_text, int3
 std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits, int32_t vocab,
                         std_dtype_t logits_dtype, int32_t* out_tokens, int32_t* n_out,
                         float* margins_or_null, int32_t* seq_len_inout_or_null, void* stream) {
-  return std_accept_batch(draft, gamma, 1, logits, vocab, logits_dtype, out_tokens, n_out,
-                          margins_or_null, seq_len_inout_or_null, stream);
+  return std_accept_batch(draft, gamma, 1, nullptr, logits, vocab, logits_dtype, out_tokens,
+                          n_out, margins_or_null, seq_len_inout_or_null, stream);
 }
 
 std_status_t std_accept_batch(const int32_t* draft, int32_t gamma, int32_t batch,
-                              const void* logits, int32_t vocab, std_dtype_t logits_dtype,
-                              int32_t* out_tokens, int32_t* n_out, float* margins_or_null,
-                              int32_t* seq_len_inout_or_null, void* stream) {
+                              const int32_t* gamma_dev_or_null, const void* logits, int32_t vocab,
+                              std_dtype_t logits_dtype, int32_t* out_tokens, int32_t* n_out,
+                              float* margins_or_null, int32_t* seq_len_inout_or_null,
+                              void* stream) {
   CHECK(gamma >= 0 && gamma < (1 << 20), STD_ERR_INVALID_ARGUMENT, "gamma %d out of range",
         gamma);
   CHECK(batch >= 1 && (long long)batch * (gamma + 1) <= 0x7fffffffLL, STD_ERR_INVALID_ARGUMENT,
@@ -416,7 +426,7 @@ std_status_t std_accept_batch(const int32_t* draft, int32_t gamma, int32_t batch
         "logits / out_tokens / n_out is null");
   CHECK(logits_dtype == STD_DTYPE_F32 || logits_dtype == STD_DTYPE_BF16,
         STD_ERR_INVALID_ARGUMENT, "unknown logits dtype %d", (int)logits_dtype);
-  return hip_status(launch_accept(draft, gamma, batch, logits, vocab,
+  return hip_status(launch_accept(draft, gamma, batch, gamma_dev_or_null, logits, vocab,
                                   logits_dtype == STD_DTYPE_BF16, out_tokens, n_out,
                                   margins_or_null, seq_len_inout_or_null,
                                   static_cast<hipStream_t>(stream)));
@@ -477,6 +487,24 @@ std_status_t std_check_idx(const int32_t* idx, int32_t n_kv_heads, int32_t topk,
   CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
   return hip_status(launch_check_idx(idx, n_kv_heads, topk, vis.vis_start, vis.vis_len, bad_out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------ streaming comparator
+
+std_status_t std_static_window_idx(int32_t n_kv_heads, std_vis_t vis, int32_t sink, int32_t topk,
+                                   int32_t* idx_out, void* stream) {
+  CHECK(n_kv_heads >= 1, STD_ERR_INVALID_ARGUMENT, "n_kv_heads must be >= 1");
+  CHECK(vis.vis_start >= 0 && vis.vis_len >= 1 &&
+            (long long)vis.vis_start + vis.vis_len <= 0x7fffffffLL,
+        STD_ERR_INVALID_ARGUMENT, "bad visual span [%d, +%d)", vis.vis_start, vis.vis_len);
+  CHECK(topk >= 0 && topk <= vis.vis_len, STD_ERR_INVALID_ARGUMENT,
+        "need 0 <= topk (%d) <= vis_len (%d)", topk, vis.vis_len);
+  CHECK(sink >= 0, STD_ERR_INVALID_ARGUMENT, "need sink (%d) >= 0", sink);
+  CHECK((long long)n_kv_heads * topk <= 0x7fffffffLL, STD_ERR_INVALID_ARGUMENT,
+        "n_kv_heads * topk too large");
+  CHECK(topk == 0 || idx_out, STD_ERR_INVALID_ARGUMENT, "idx_out is null");
+  return hip_status(launch_static_window_idx(n_kv_heads, vis.vis_start, vis.vis_len, sink, topk,
+                                             idx_out, static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------ read probe

@@ -49,20 +49,24 @@ struct KeyList {
 };
 
 // Valid cache length of a call: the host value, or (device-length calls)
-// min(max(*dev + off, 1), max) read when the kernel runs, so a decode loop
+// min(max(*dev + off, lo), max) read when the kernel runs, so a decode loop
 // captured once in a graph sees the length the previous step committed.
-// ptr() never is null (a zero word stands in for a missing device length),
-// so a kernel can load it as a vector load issued with its first memory
-// accesses and apply resolve() where the length is first needed.
+// lo is the shortest length the call is defined for (dense: n_q, so every
+// query row sees at least one key; sparse: the end of the visual span, or
+// one past it when the key list would otherwise be empty); the host checks
+// lo <= max.  ptr() never is null (a zero word stands in for a missing
+// device length), so a kernel can load it as a vector load issued with its
+// first memory accesses and apply resolve() where the length is first needed.
 __device__ int32_t kNoDeviceLen = 0;
 struct LenSrc {
   int max;
   const int32_t* dev;
   int off;
-  __device__ __forceinline__ int get() const { return dev ? min(max_(*dev + off, 1), max) : max; }
+  int lo;
+  __device__ __forceinline__ int get() const { return dev ? min(max_(*dev + off, lo), max) : max; }
   __device__ __forceinline__ const int32_t* ptr() const { return dev ? dev : &kNoDeviceLen; }
   __device__ __forceinline__ int resolve(int d) const {
-    return dev ? min(max_(d + off, 1), max) : max;
+    return dev ? min(max_(d + off, lo), max) : max;
   }
   static __device__ __forceinline__ int max_(int a, int b) { return a > b ? a : b; }
 };
@@ -435,7 +439,8 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, LenSrc lsrc,
-    int splits, int rows_total, float2* __restrict__ ml, float* __restrict__ o) {
+    const int32_t* __restrict__ gamma_dev, int step, int splits, int rows_total,
+    float2* __restrict__ ml, float* __restrict__ o) {
   constexpr int EW = kSparseEntriesPerWave;
   constexpr int NKB = EW / 16;
   using TM = TileMath<D, NKB>;
@@ -451,6 +456,9 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;   // split, KV head, sequence
+  // a sequence whose own draft length ends before this step drafts nothing
+  // (the whole workgroup leaves; the combine skips its rows likewise)
+  if (gamma_dev && gamma_dev[b] <= step) return;
   // sequence b of a batch: its query rows, cache, index list and length
   q += (size_t)b * hq * D;
   k += (size_t)b * hkv * capacity * D;
@@ -673,12 +681,14 @@ constexpr int kCombineBatch = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float2* __restrict__ ml, const float* __restrict__ o, int splits, int rows,
-    T* __restrict__ out) {
+    T* __restrict__ out, const int32_t* __restrict__ gamma_dev, int step, int rows_per_seq) {
   constexpr int DQ = D / 4;                      // float4 columns
   constexpr int NSG = kCombineThreads / DQ;      // split groups
   __shared__ float4 part[NSG][DQ];
   __shared__ float2 stat[NSG][DQ];
   const int r = blockIdx.x, tid = threadIdx.x;
+  // rows of a sequence that drafts nothing in this step keep their output
+  if (gamma_dev && gamma_dev[r / rows_per_seq] <= step) return;
   const int dq = tid % DQ, sg = tid / DQ;
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -742,10 +752,13 @@ hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
   const int rows = (a.batch > 1 ? a.batch : 1) * a.n_q * a.hq;
   const auto* mlp = reinterpret_cast<const float2*>(a.ml);
   T* out = static_cast<T*>(a.out);
+  const int rps = a.n_q * a.hq;                  // rows of one sequence
   if (a.d == 128)
-    combine_kernel<T, 128><<<rows, kCombineThreads, 0, st>>>(mlp, a.o, a.splits, rows, out);
+    combine_kernel<T, 128><<<rows, kCombineThreads, 0, st>>>(mlp, a.o, a.splits, rows, out,
+                                                             a.gamma_dev, a.step, rps);
   else
-    combine_kernel<T, 64><<<rows, kCombineThreads, 0, st>>>(mlp, a.o, a.splits, rows, out);
+    combine_kernel<T, 64><<<rows, kCombineThreads, 0, st>>>(mlp, a.o, a.splits, rows, out,
+                                                            a.gamma_dev, a.step, rps);
   return hipGetLastError();
 }
 
@@ -755,7 +768,8 @@ hipError_t launch_valu(const AttnArgs& a, const KeyList& kl, hipStream_t st) {
   dim3 grid(rows_group, a.hkv, a.splits);
   attn_valu_kernel<T, D><<<grid, 64, 0, st>>>(
       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-      a.hq, a.hkv, a.capacity, LenSrc{a.len, a.len_dev, a.len_off}, a.n_q, a.scale * kLog2e, kl,
+      a.hq, a.hkv, a.capacity, LenSrc{a.len, a.len_dev, a.len_off, a.len_lo}, a.n_q,
+      a.scale * kLog2e, kl,
       a.chunk, reinterpret_cast<float2*>(a.ml), a.o, a.n_q * a.hq);
   return hipGetLastError();
 }
@@ -766,12 +780,13 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const float c = a.scale * kLog2e;
-  const LenSrc lsrc{a.len, a.len_dev, a.len_off};
+  const LenSrc lsrc{a.len, a.len_dev, a.len_off, a.len_lo};
   if (a.sparse) {
     const int batch = a.batch > 1 ? a.batch : 1;
     sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv, batch), 64 * kSparseWaves, 0, st>>>(
         q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
-        a.topk, lsrc, a.splits, batch * a.hq, reinterpret_cast<float2*>(a.ml), a.o);
+        a.topk, lsrc, a.gamma_dev, a.step, a.splits, batch * a.hq,
+        reinterpret_cast<float2*>(a.ml), a.o);
   } else {
     const int batch = a.batch > 1 ? a.batch : 1;
     const int rows_group = a.n_q * (a.hq / a.hkv);

@@ -80,6 +80,11 @@ struct AttnArgs {
   // (sparse batch: len_dev[b] for sequence b)
   const int32_t* len_dev;
   int len_off;
+  int len_lo;           // shortest valid length a device value resolves to
+  // per-sequence draft lengths (sparse batch only, else null): sequence b
+  // takes part in draft step `step` only while step < gamma_dev[b]
+  const int32_t* gamma_dev;
+  int step;
   // independent sequences laid out back to back (q, out [batch][n_q][Hq][D],
   // K and V [batch][Hkv][capacity][D], sparse idx [batch][Hkv][topk],
   // len_dev[b]); 0 or 1: one sequence
@@ -119,8 +124,16 @@ size_t select_workspace_bytes(int hq, int hkv, int d, int n_text, int vis_len,
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
 // Acceptance (accept.hip).
-hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const void* logits, int vocab,
-                         bool bf16, int32_t* out_tokens, int32_t* n_out, float* margins,
-                         int32_t* seq_len, hipStream_t stream);
+// gamma is the row stride ([batch][gamma] drafts, [batch][gamma+1] logit
+// rows); gamma_dev (null: every sequence uses gamma) holds each sequence's
+// own draft length, clamped into [0, gamma].
+hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const int32_t* gamma_dev,
+                         const void* logits, int vocab, bool bf16, int32_t* out_tokens,
+                         int32_t* n_out, float* margins, int32_t* seq_len, hipStream_t stream);
+
+// Streaming-baseline index lists (check.hip): [n_kv_heads][topk] positions,
+// the first min(sink, topk) of the span then its last topk - min(sink, topk).
+hipError_t launch_static_window_idx(int n_kv_heads, int vis_start, int vis_len, int sink,
+                                    int topk, int32_t* idx_out, hipStream_t stream);
 
 }  // namespace stdspec

@@ -9,7 +9,9 @@ goes through the library:
                     (bottom-right causal alignment makes a chunk of n_q rows
                     ending at position p the causal rows of the prompt);
 * selection      -- std_select_topk per layer on the prefill's rotated text
-                    queries (technical summary, Methodology item 4);
+                    queries (technical summary, Methodology item 4), or the
+                    streaming comparator's fixed lists (std_static_window_idx:
+                    an attention sink plus a recent window of the visual span);
 * draft step     -- std_sparse_decode_attn, one token at a time, over the
                     selected visual KV plus all other KV (Methodology item 2);
 * verify         -- std_dense_verify_attn with the gamma+1 queries
@@ -39,23 +41,29 @@ class ToyDecoder:
     per layer ``attn_norm, wq, wk, wv, wo, mlp_norm, w_gate, w_up, w_down``
     (matrices as [in][out]), ``final_norm`` and ``lm_head [hidden][vocab]``,
     plus ``cfg`` with n_q_heads, n_kv_heads, head_dim, eps and rope_theta.
-    ``dtype`` is the cache and matmul type (bf16 or fp32); norms, the
-    residual stream and the logits stay in fp32.
+    ``dtype`` is the cache and attention type (bf16 or fp32) and, unless
+    ``matmul_dtype`` says otherwise, the projections' type; norms, the
+    residual stream and the logits stay in fp32.  fp32 projections beside a
+    bf16 cache keep the model's rows independent of how many rows a forward
+    takes (a torch GEMM over 1 row and over gamma+1 rows may round
+    differently), so a bf16-attention draft-verify loop can be compared
+    token for token with bf16-attention greedy decoding.
     """
 
     def __init__(self, params, capacity, device="cuda", dtype=torch.bfloat16,
-                 prefill_chunk=512):
+                 prefill_chunk=512, matmul_dtype=None):
         cfg = params["cfg"]
         self.cfg = cfg
         self.hq, self.hkv, self.d = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
         self.eps = float(cfg["eps"])
         self.dt = dtype
+        self.mt = dtype if matmul_dtype is None else matmul_dtype
         self.dev = torch.device(device)
         self.capacity = int(capacity)
         self.chunk = int(prefill_chunk)
 
         def mat(a):
-            return torch.as_tensor(a, dtype=dtype, device=self.dev).contiguous()
+            return torch.as_tensor(a, dtype=self.mt, device=self.dev).contiguous()
 
         def vec(a):
             return torch.as_tensor(a, dtype=torch.float32, device=self.dev).contiguous()
@@ -129,10 +137,10 @@ class ToyDecoder:
         hq, hkv, d = self.hq, self.hkv, self.d
         q_text = []
         for li, lp in enumerate(self.layers):
-            h = self._rms(x, lp["attn_norm"]).to(self.dt)
+            h = self._rms(x, lp["attn_norm"]).to(self.mt)
             q = (h @ lp["wq"]).float().view(T, hq, d)
             k = (h @ lp["wk"]).float().view(T, hkv, d)
-            v = (h @ lp["wv"]).view(T, hkv, d)
+            v = (h @ lp["wv"]).to(self.dt).view(T, hkv, d)
             q = self._rope(q, pos0, T).to(self.dt).contiguous()
             k = self._rope(k, pos0, T).to(self.dt)
             self.k[li][:, pos0:length] = k.transpose(0, 1)
@@ -149,8 +157,8 @@ class ToyDecoder:
                 o = _lib.std_sparse_decode_attn(q[0], self.k[li], self.v[li], length, vis_start,
                                                 vis_len, idx[li], workspace=self._sparse_ws(
                                                     idx[li].shape[1], vis_start, vis_len))[None]
-            x = x + (o.reshape(T, hq * d) @ lp["wo"]).float()
-            h = self._rms(x, lp["mlp_norm"]).to(self.dt)
+            x = x + (o.reshape(T, hq * d).to(self.mt) @ lp["wo"]).float()
+            h = self._rms(x, lp["mlp_norm"]).to(self.mt)
             g = torch.nn.functional.silu(h @ lp["w_gate"])
             x = x + ((g * (h @ lp["w_up"])) @ lp["w_down"]).float()
         logits = self._rms(x, self.final_norm) @ self.lm_head
@@ -194,6 +202,14 @@ class ToyDecoder:
         return [_lib.std_select_topk(q_text[li], self.k[li], prompt_len, prompt_len - n_text,
                                      vis_start, vis_len, topk, workspace=ws)
                 for li in range(len(self.layers))]
+
+    def select_static(self, vis_start, vis_len, sink, topk):
+        """The streaming comparator's visual positions, the same for every
+        layer: the first min(sink, topk) and the last topk - min(sink, topk)
+        of the span (std_static_window_idx)."""
+        idx = _lib.std_static_window_idx(self.hkv, vis_start, vis_len, sink, topk,
+                                         device=self.dev)
+        return [idx for _ in self.layers]
 
     def snapshot(self):
         return [t.clone() for t in self.k + self.v]

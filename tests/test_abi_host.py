@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.std_abi_version() == 1
+    assert lib.std_abi_version() == 2
     assert lib.std_status_str(0) == b"STD_OK"
     assert lib.std_status_str(3) == b"STD_ERR_WORKSPACE_TOO_SMALL"
     assert lib.std_status_str(99) == b"STD_ERR_UNKNOWN"
@@ -134,12 +134,12 @@ def test_batched_sparse_decode_rejects():
     sh = _shape()
     P = ctypes.c_void_p
 
-    def call(batch=4, kv=None, topk=64, len_dev=0):
+    def call(batch=4, kv=None, topk=64, len_dev=0, gamma_dev=0, step=0):
         kv = kv or _kv()
         return lib.std_sparse_decode_attn_batch(ctypes.byref(sh), P(FAKE), batch,
                                                 ctypes.byref(kv), P(len_dev), 0,
-                                                _lib.Vis(0, 800), P(FAKE), topk, P(FAKE), None, 0,
-                                                None)
+                                                _lib.Vis(0, 800), P(FAKE), topk, P(gamma_dev),
+                                                step, P(FAKE), None, 0, None)
 
     E = _lib.STD_ERR_INVALID_ARGUMENT
     assert call(batch=0) == E
@@ -148,6 +148,8 @@ def test_batched_sparse_decode_rejects():
     assert call(kv=_kv(dtype=_lib.STD_DTYPE_F32)) == _lib.STD_ERR_UNSUPPORTED
     assert call() == _lib.STD_ERR_WORKSPACE_TOO_SMALL
     assert call(len_dev=FAKE) == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert call(gamma_dev=FAKE, step=-1) == E            # a draft step is >= 0
+    assert call(gamma_dev=FAKE, step=3) == _lib.STD_ERR_WORKSPACE_TOO_SMALL
     assert call(batch=1, kv=_kv(dtype=_lib.STD_DTYPE_F32)) == _lib.STD_ERR_WORKSPACE_TOO_SMALL
     one = lib.std_sparse_decode_batch_workspace(ctypes.byref(sh), 1, ctypes.byref(_kv()),
                                                 _lib.Vis(0, 800), 64)
@@ -234,10 +236,10 @@ def test_batched_verify_and_accept_reject():
     two = lib.std_dense_verify_batch_workspace(ctypes.byref(sh), 6, 2, ctypes.byref(_kv()))
     assert one > 0 and two > one
     # acceptance: every check fires before a launch
-    assert lib.std_accept_batch(p, 3, 0, p, 10, 0, p, p, None, None, None) == E
-    assert lib.std_accept_batch(p, -1, 2, p, 10, 0, p, p, None, None, None) == E
-    assert lib.std_accept_batch(None, 3, 2, p, 10, 0, p, p, None, None, None) == E
-    assert lib.std_accept_batch(p, 3, 2, p, 10, 7, p, p, None, None, None) == E
+    assert lib.std_accept_batch(p, 3, 0, None, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept_batch(p, -1, 2, None, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept_batch(None, 3, 2, None, p, 10, 0, p, p, None, None, None) == E
+    assert lib.std_accept_batch(p, 3, 2, p, p, 10, 7, p, p, None, None, None) == E
 
 
 def test_check_idx_rejects():
@@ -322,3 +324,116 @@ def test_workspace_queries_follow_their_calls():
     assert "kv is null" in reason()
     assert lib.std_prefill_text_attn_workspace(ctypes.byref(sh), -1, 10) == 0
     assert "text_start" in reason()
+
+
+def test_static_window_idx_rejects():
+    lib = _lib.load()
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+    p = ctypes.c_void_p(FAKE)
+    vis = _lib.Vis(0, 100)
+    assert lib.std_static_window_idx(0, vis, 4, 10, p, None) == E
+    assert lib.std_static_window_idx(2, _lib.Vis(-1, 100), 4, 10, p, None) == E
+    assert lib.std_static_window_idx(2, _lib.Vis(0, 0), 4, 10, p, None) == E
+    assert lib.std_static_window_idx(2, vis, 4, 101, p, None) == E
+    assert lib.std_static_window_idx(2, vis, 4, -1, p, None) == E
+    assert lib.std_static_window_idx(2, vis, -1, 10, p, None) == E
+    assert lib.std_static_window_idx(2, vis, 4, 10, None, None) == E
+    assert lib.std_static_window_idx(2, _lib.Vis(0x7fffff00, 0x1000), 4, 10, p, None) == E
+    assert lib.std_last_error() != b""
+
+
+# ------------------------------------------------------- binding validation
+# The Python wrappers check dtypes and shapes before the device, so these
+# rejections are reachable with CPU tensors; nothing reaches the library.
+
+import torch  # noqa: E402
+
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+def _raises(fn, what):
+    with pytest.raises(ValueError) as e:
+        fn()
+    assert what in str(e.value), str(e.value)
+
+
+def test_binding_rejects_mismatched_attention_tensors():
+    k, v = _t(4, 300, 128), _t(4, 300, 128)
+    q = _t(7, 28, 128)
+    _raises(lambda: _lib.std_dense_verify_attn(q.float(), k, v, 200), "q must be")
+    _raises(lambda: _lib.std_dense_verify_attn(q, k, _t(4, 299, 128), 200), "v must have shape")
+    _raises(lambda: _lib.std_dense_verify_attn(q, k, v.float(), 200), "v must be")
+    _raises(lambda: _lib.std_dense_verify_attn(_t(7, 28, 64), k, v, 200), "head_dim 128")
+    _raises(lambda: _lib.std_dense_verify_attn(q, k, v, 200, out=_t(7, 28, 128).float()),
+            "out must be")
+    _raises(lambda: _lib.std_dense_verify_attn(q, k, v, 200, out=_t(6, 28, 128)),
+            "out must have shape")
+    _raises(lambda: _lib.std_dense_verify_attn(q, _t(4, 300, 128, dtype=torch.float16), v, 200),
+            "k must be")
+    qs = _t(28, 128)
+    idx = torch.zeros(4, 16, dtype=torch.int32)
+    _raises(lambda: _lib.std_sparse_decode_attn(qs, k, v, 200, 0, 100, idx.long()),
+            "idx must be")
+    _raises(lambda: _lib.std_sparse_decode_attn(qs, k, v, 200, 0, 100, idx[:3]), "idx must be")
+    _raises(lambda: _lib.std_sparse_decode_attn(qs, k, v, 200, 0, 100, idx,
+                                                out=_t(28, 64)), "out must have shape")
+    _raises(lambda: _lib.std_sparse_decode_attn_dlen(qs, k, v, 200, torch.zeros(1), 0, 0, 100,
+                                                     idx), "len_dev must be")
+    kb, vb = _t(2, 4, 300, 128), _t(2, 4, 300, 128)
+    _raises(lambda: _lib.std_sparse_decode_attn_batch(_t(3, 28, 128), kb, vb, 200, 0, 100,
+                                                      torch.zeros(3, 4, 16, dtype=torch.int32)),
+            "same batch")
+    _raises(lambda: _lib.std_sparse_decode_attn_batch(
+        _t(2, 28, 128), kb, vb, 200, 0, 100, torch.zeros(2, 4, 16, dtype=torch.int32),
+        gamma_dev=torch.zeros(3, dtype=torch.int32)), "gamma_dev must have shape")
+    _raises(lambda: _lib.std_dense_verify_attn_batch(_t(2, 7, 28, 128), kb, vb, 200,
+                                                     len_dev=torch.zeros(3, dtype=torch.int32)),
+            "len_dev must hold 2")
+
+
+def test_binding_rejects_bad_selection_and_prefill_buffers():
+    k, v = _t(4, 300, 128), _t(4, 300, 128)
+    qt = _t(28, 20, 128)
+    _raises(lambda: _lib.std_select_topk(qt, k, 280, 260, 0, 200, 16,
+                                         lse=torch.zeros(28 * 19)), "lse must hold")
+    _raises(lambda: _lib.std_select_topk(qt, k, 280, 260, 0, 200, 16,
+                                         lse=torch.zeros(28, 20, dtype=torch.float64)),
+            "lse must be")
+    _raises(lambda: _lib.std_select_topk(qt, k, 280, 260, 0, 200, 16,
+                                         idx_out=torch.zeros(4, 15, dtype=torch.int32)),
+            "idx_out must have shape")
+    _raises(lambda: _lib.std_select_topk(qt, k, 280, 260, 0, 200, 16,
+                                         scores_out=torch.zeros(4, 199)),
+            "scores_out must have shape")
+    _raises(lambda: _lib.std_select_topk(qt.float(), k, 280, 260, 0, 200, 16), "q_text must be")
+    _raises(lambda: _lib.std_prefill_text_attn(qt, k, v, 280, 260, lse_out=torch.zeros(28, 19)),
+            "lse_out must be")
+    _raises(lambda: _lib.std_prefill_text_attn(qt, k, v, 280, 260, out=_t(28, 19, 128)),
+            "out must have shape")
+
+
+def test_binding_rejects_bad_acceptance_buffers():
+    draft = torch.zeros(4, dtype=torch.int32)
+    logits = torch.zeros(5, 100)
+    _raises(lambda: _lib.std_accept(draft, torch.zeros(4, 100)), "logits must be")
+    _raises(lambda: _lib.std_accept(draft.long(), logits), "draft must be")
+    _raises(lambda: _lib.std_accept(draft, logits.double()), "logits must be")
+    _raises(lambda: _lib.std_accept(draft, logits, out_tokens=torch.zeros(4, dtype=torch.int32)),
+            "out_tokens must have shape")
+    _raises(lambda: _lib.std_accept(draft, logits, margins=torch.zeros(4)), "margins must have")
+    _raises(lambda: _lib.std_accept(draft, logits, n_out=torch.zeros(0, dtype=torch.int32)),
+            "n_out must hold")
+    _raises(lambda: _lib.std_accept(draft, logits, seq_len=torch.zeros(1)), "seq_len must be")
+    db = torch.zeros(3, 4, dtype=torch.int32)
+    _raises(lambda: _lib.std_accept_batch(db, torch.zeros(3, 4, 100)), "logits must be")
+    _raises(lambda: _lib.std_accept_batch(db, torch.zeros(3, 5, 100),
+                                          n_out=torch.zeros(2, dtype=torch.int32)),
+            "n_out must hold")
+    _raises(lambda: _lib.std_accept_batch(db, torch.zeros(3, 5, 100),
+                                          gamma_dev=torch.zeros(2, dtype=torch.int32)),
+            "gamma_dev must have shape")
+    _raises(lambda: _lib.std_static_window_idx(4, 0, 100, 8, 16,
+                                               idx_out=torch.zeros(4, 15, dtype=torch.int32)),
+            "idx_out must have shape")

@@ -177,3 +177,83 @@ def test_batched_cycle_equals_single_calls(lib):
             assert torch.equal(drafts_b[j][b], one), (b, j)
         ref = oracle.dense_verify(f64(qv[b]), f64(kb), f64(vb), ctx[b] + gamma + 1)
         assert np.max(np.abs(f64(verify_b[b]) - ref)) <= TOL, b
+
+
+# ------------------------------------------------ per-sequence draft lengths
+def test_batched_accept_per_sequence_gamma(lib):
+    """Each sequence's own gamma_b (a device array; gamma is the row stride):
+    sequence b is std_accept on draft[b][:gamma_b] and logit rows
+    [b][:gamma_b + 1], against the oracle; unused slots are -1 and unused
+    rows' margins NaN; each length advances by its own n + 1."""
+    import synth
+    B, stride, vocab = 6, 6, 2000
+    gam = [6, 0, 3, 1, 6, 4]
+    cases = [synth.accept_case(stride, vocab, 0.85, seed=90 + b, dtype=torch.bfloat16,
+                               n_ties=b % 2) for b in range(B)]
+    draft = torch.stack([c[0] for c in cases]).cuda()
+    logits = torch.stack([c[1] for c in cases]).contiguous().cuda()
+    gdev = torch.tensor(gam, dtype=torch.int32, device="cuda")
+    seq = torch.tensor([10 * b for b in range(B)], dtype=torch.int32, device="cuda")
+    margins = torch.zeros(B, stride + 1, dtype=torch.float32, device="cuda")
+    toks, n_out = lib.std_accept_batch(draft, logits, seq_len=seq, margins=margins,
+                                       gamma_dev=gdev)
+    torch.cuda.synchronize()
+    m = margins.cpu().numpy()
+    for b in range(B):
+        g = gam[b]
+        ref_toks, ref_n, ref_m, _ = oracle.accept(cases[b][0][:g].numpy(),
+                                                  f64(cases[b][1][:g + 1]))
+        got = toks[b].cpu().numpy().tolist()
+        assert got[:g + 1] == ref_toks.tolist(), b
+        assert got[g + 1:] == [-1] * (stride - g), b
+        assert int(n_out[b]) == ref_n and 1 <= ref_n <= g + 1
+        assert int(seq[b]) == 10 * b + ref_n
+        assert np.allclose(m[b, :g + 1], ref_m, rtol=0, atol=1e-6)
+        assert np.all(np.isnan(m[b, g + 1:]))
+    # with every gamma_b equal to the stride the call is the uniform one
+    full = torch.full((B,), stride, dtype=torch.int32, device="cuda")
+    t1, n1 = lib.std_accept_batch(draft, logits, gamma_dev=full)
+    t2, n2 = lib.std_accept_batch(draft, logits)
+    torch.cuda.synchronize()
+    assert torch.equal(t1, t2) and torch.equal(n1, n2)
+
+
+def test_batched_cycle_per_sequence_gamma(lib):
+    """A cycle for three sequences drafting 4, 2 and 3 tokens: draft step j
+    runs only the sequences with j < gamma_b (bit for bit the single
+    device-length call; the others' output rows stay untouched); the verify
+    pass takes 1 + max gamma queries and sequence b's first gamma_b + 1 rows
+    are its verify rows (against the oracle); acceptance per sequence."""
+    B, hq, hkv, d, vis_len, topk = 3, 28, 4, 128, 1500, 128
+    gam = (4, 2, 3)
+    gmax = max(gam)
+    ctx = (1700, 1601, 1800)
+    cap = max(ctx) + gmax + 2
+    q, k, v, idx = make_batch(B, hq, hkv, d, 0, vis_len, cap, topk, seed=77)
+    g = torch.Generator(device="cpu").manual_seed(76)
+    qv = (torch.randn(B, gmax + 1, hq, d, generator=g) * 1.5).bfloat16().cuda()
+    seq = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    gdev = torch.tensor(gam, dtype=torch.int32, device="cuda")
+    sentinel = torch.full_like(q, 7.0)
+    drafts = []
+    for j in range(gmax):
+        o = sentinel.clone()
+        lib.std_sparse_decode_attn_batch(q, k, v, cap, 0, vis_len, idx, len_dev=seq,
+                                         len_offset=1 + j, gamma_dev=gdev, step=j, out=o)
+        drafts.append(o)
+    verify = lib.std_dense_verify_attn_batch(qv, k, v, cap, len_dev=seq, len_offset=gmax + 1)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kb, vb = k[b].contiguous(), v[b].contiguous()
+        for j in range(gmax):
+            if j < gam[b]:
+                one = lib.std_sparse_decode_attn_dlen(q[b].contiguous(), kb, vb, cap,
+                                                      seq[b:b + 1], 1 + j, 0, vis_len,
+                                                      idx[b].contiguous())
+                torch.cuda.synchronize()
+                assert torch.equal(drafts[j][b], one), (b, j)
+            else:
+                assert torch.equal(drafts[j][b], sentinel[b]), (b, j)
+        rows = gam[b] + 1
+        ref = oracle.dense_verify(f64(qv[b][:rows]), f64(kb), f64(vb), ctx[b] + rows)
+        assert np.max(np.abs(f64(verify[b][:rows]) - ref)) <= TOL, b

@@ -152,3 +152,39 @@ def test_graph_replayed_cycle(lib, c2):
         assert int(n_out.item()) == ref_n
         assert int(seq.item()) == t + ref_n, "the accept step advances the device length"
         say(f"replay {rep}: t={t} -> {int(seq.item())}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_dlen_below_the_shortest_length_is_raised_to_it(lib, dtype):
+    """A device length shorter than the call is defined for resolves to the
+    shortest defined length (dense: n_q, so every query row sees a key;
+    sparse: the end of the visual span, one past it when the key list would
+    otherwise be empty), so the output is a defined attention result, never
+    NaN."""
+    g = torch.Generator(device="cpu").manual_seed(21)
+    hq, hkv, d, vis_len, cap, n_q, topk = 8, 2, 128, 300, 400, 7, 32
+    k = torch.randn(hkv, cap, d, generator=g).to(dtype)
+    v = torch.randn(hkv, cap, d, generator=g).to(dtype)
+    qv = torch.randn(n_q, hq, d, generator=g).to(dtype)
+    q1 = torch.randn(hq, d, generator=g).to(dtype)
+    idx = torch.stack([torch.sort(torch.randperm(vis_len, generator=g)[:topk])[0]
+                       for _ in range(hkv)]).to(torch.int32)
+    kc, vc, qvc, q1c, idxc = (t.cuda() for t in (k, v, qv, q1, idx))
+    kf, vf = f64(k), f64(v)
+    tol = 1e-5 if dtype == torch.float32 else TOL
+    for dev_len in (-50, 0, 3):
+        seq = torch.tensor([dev_len], dtype=torch.int32, device="cuda")
+        outv = lib.std_dense_verify_attn_dlen(qvc, kc, vc, cap, seq, 0)
+        out_s = lib.std_sparse_decode_attn_dlen(q1c, kc, vc, cap, seq, 1, 0, vis_len, idxc)
+        out_0 = lib.std_sparse_decode_attn_dlen(q1c, kc, vc, cap, seq, 1, 0, vis_len,
+                                                idxc[:, :0].contiguous())
+        torch.cuda.synchronize()
+        say(f"{dtype} device length {dev_len}")
+        for o in (outv, out_s, out_0):
+            assert torch.isfinite(o.float()).all()
+        assert max_abs(f64(outv), oracle.dense_verify(f64(qv), kf, vf, n_q)) <= tol
+        ref_s = oracle.sparse_decode(f64(q1), kf, vf, vis_len, 0, vis_len, idx.numpy())
+        assert max_abs(f64(out_s), ref_s) <= tol
+        ref_0 = oracle.sparse_decode(f64(q1), kf, vf, vis_len + 1, 0, vis_len,
+                                     np.zeros((hkv, 0), np.int64))
+        assert max_abs(f64(out_0), ref_0) <= tol

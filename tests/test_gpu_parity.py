@@ -279,21 +279,16 @@ def test_select_topk_shapes(lib, hq, hkv, d, prefix, vis_len, n_text, topk):
 
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_select_topk_uses_caller_lse(lib, name):
-    """The caller's natural-log row LSE replaces step 1 (fp32 and bf16 paths)."""
+    """The caller's natural-log row LSE replaces step 1 (fp32 and bf16 paths).
+    The LSE comes from the oracle's own row normaliser (row_lse), the value a
+    prefill attention returns beside its output."""
     cfg = synth.config(name)
     lay = layer(cfg)
-    # the natural-log LSE of each text row (all keys up to its own position)
+    # text row i of head h sits at position text_start + i: the rows of a
+    # dense pass of n_text queries ending at text_start + n_text
     qf, kf = f64(lay["q_text"]), f64(lay["k"])
-    G = cfg.n_q_heads // cfg.n_kv_heads
-    n_keys = cfg.text_start + cfg.n_text
-    keypos = np.arange(n_keys)[:, None]
-    rowpos = cfg.text_start + np.arange(cfg.n_text)[None, :]
-    lse = np.empty((cfg.n_q_heads, cfg.n_text))
-    for h in range(cfg.n_q_heads):
-        s = (kf[h // G, :n_keys] @ qf[h].T) / np.sqrt(cfg.head_dim)   # [keys][rows]
-        s = np.where(keypos <= rowpos, s, -np.inf)
-        mx = s.max(axis=0)
-        lse[h] = mx + np.log(np.exp(s - mx).sum(axis=0))
+    lse = np.ascontiguousarray(
+        oracle.row_lse(qf.transpose(1, 0, 2), kf, cfg.text_start + cfg.n_text).T)
     lse_t = torch.from_numpy(lse.astype(np.float32)).cuda()
     idx, scores = lib.std_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
                                       cfg.vis_start, cfg.vis_len, cfg.topk, lse=lse_t,

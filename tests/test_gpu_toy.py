@@ -71,15 +71,22 @@ def test_dense_stream_matches_oracle_greedy(setup):
     assert s["dense"][:n] == ref[:n]
 
 
-@pytest.mark.parametrize("topk,gamma", [(64, 4), (16, 2), (256, 6)])
-def test_std_stream_equals_dense_stream(setup, topk, gamma):
+@pytest.mark.parametrize("topk,gamma,sink", [(64, 4, None), (16, 2, None), (256, 6, None),
+                                             (64, 4, 8)])
+def test_std_stream_equals_dense_stream(setup, topk, gamma, sink):
+    """sink None: the attention-ranked top-K lists; a sink size: the
+    streaming comparator's lists (sink + recent window) through the same
+    draft call.  Either way the output is the dense model's."""
     s = setup
     cfg, dec = s["cfg"], s["dec"]
     dec.restore(s["snap"])
-    idx = dec.select(s["q_text"], s["prompt_len"], 0, cfg["n_vis"], topk)
+    if sink is None:
+        idx = dec.select(s["q_text"], s["prompt_len"], 0, cfg["n_vis"], topk)
+    else:
+        idx = dec.select_static(0, cfg["n_vis"], sink, topk)
     out, acc = dec.decode_std(s["first"], s["prompt_len"], N_NEW, idx, 0, cfg["n_vis"], gamma)
     n = trusted_prefix(s["margins"])
-    say(f"K={topk} gamma={gamma}: accepted per cycle {acc}; trusted prefix {n}")
+    say(f"K={topk} gamma={gamma} sink={sink}: accepted per cycle {acc}; trusted prefix {n}")
     assert all(0 <= a <= gamma for a in acc)
     assert out[:n] == s["dense"][:n]
 
@@ -103,3 +110,72 @@ def test_full_selection_accepts_every_draft(setup):
             break
         assert a == gamma
         pos += a + 1
+
+
+
+# ------------------------------------------------------------------ bf16
+# The toy decoder of the long-video toy workload (4 layers, hidden 512,
+# 8/2/64, vocab 8,192, K = 512) with a bf16 cache, so every attention runs on
+# the bf16 MFMA kernels the benchmark uses; projections in fp32 keep each row
+# independent of the forward's row count.  Weights N(0, 0.04^2) make the
+# attention peaked enough that the top-K draft departs from the dense model
+# now and then: cycles accept anything from 0 to gamma drafts.
+N_NEW_BF16 = 96
+
+
+@pytest.fixture(scope="module")
+def setup_bf16():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_draft_speculative_amd as sd
+    from sparse_draft_speculative_amd.toy_decoder import ToyDecoder
+    sd.load()
+    cfg = dict(synth.TOY_C5)
+    params = synth.toy_params(cfg, seed=0, std=0.04)
+    vis, text = synth.toy_prompt(cfg, seed=0)
+    prompt_len = cfg["n_vis"] + cfg["n_text"]
+    dec = ToyDecoder(params, prompt_len + N_NEW_BF16 + 16, dtype=torch.bfloat16,
+                     matmul_dtype=torch.float32, prefill_chunk=512)
+    margins = torch.full((N_NEW_BF16,), float("inf"), dtype=torch.float32, device="cuda")
+    first, q_text = dec.prefill(vis, text, margin=margins[0:1])
+    snap = dec.snapshot()
+    dense = dec.decode_dense(first, prompt_len, N_NEW_BF16, margins=margins)
+    torch.cuda.synchronize()
+    return dict(cfg=cfg, dec=dec, first=first, q_text=q_text, snap=snap, dense=dense,
+                margins=margins.cpu().numpy(), prompt_len=prompt_len)
+
+
+def cycles_inside(acc, gamma, n_trusted):
+    """Accepted counts of the cycles whose tokens all lie in the trusted
+    prefix (the stream's token 0 comes from the prefill)."""
+    out, pos = [], 1
+    for a in acc:
+        if pos + a + 1 > n_trusted:
+            break
+        out.append(a)
+        pos += a + 1
+    return out
+
+
+@pytest.mark.parametrize("gamma,static", [(4, False), (6, False), (4, True)])
+def test_bf16_std_stream_equals_dense_stream(setup_bf16, gamma, static):
+    s = setup_bf16
+    cfg, dec = s["cfg"], s["dec"]
+    dec.restore(s["snap"])
+    if static:
+        idx = dec.select_static(0, cfg["n_vis"], 64, cfg["topk"])
+    else:
+        idx = dec.select(s["q_text"], s["prompt_len"], 0, cfg["n_vis"], cfg["topk"])
+    out, acc = dec.decode_std(s["first"], s["prompt_len"], N_NEW_BF16, idx, 0, cfg["n_vis"],
+                              gamma)
+    n = trusted_prefix(s["margins"])
+    inside = cycles_inside(acc, gamma, n)
+    say(f"bf16 gamma={gamma} static={static}: accepted per cycle {acc}; trusted prefix {n}")
+    assert n >= 32
+    assert out[:n] == s["dense"][:n]
+    assert all(0 <= a <= gamma for a in acc)
+    if not static:
+        # the stream check covers partly accepted drafts, not only all-or-none
+        # (the comparator's lists on this random-init model accept nearly
+        # every draft, so only the attention-ranked lists are held to this)
+        assert any(0 < a < gamma for a in inside), inside

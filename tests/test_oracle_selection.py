@@ -139,3 +139,51 @@ def test_generator_planted_keys_are_selected():
     planted = set(np.nonzero(lay["planted"][0].numpy())[0].tolist())
     hit = len(planted & set(idx[0].tolist()))
     assert hit >= 56, hit
+
+
+# ------------------------------------------------ streaming comparator lists
+def test_static_window_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "static_window_cases.json")))
+    for c in g["cases"]:
+        got = oracle.static_window_idx(c["vis_start"], c["vis_len"], c["sink"], c["topk"])
+        assert got.tolist() == c["idx"], c["derivation"]
+
+
+def test_static_window_invariants():
+    """A valid draft index list of K positions; the first min(sink, K) are
+    the span's first positions and the rest one run ending at the span's
+    end; brute force over every position of the span gives the same set."""
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        vis_start = int(rng.integers(0, 50))
+        vis_len = int(rng.integers(1, 80))
+        topk = int(rng.integers(0, vis_len + 1))
+        sink = int(rng.integers(0, 90))
+        got = oracle.static_window_idx(vis_start, vis_len, sink, topk)
+        assert len(got) == topk and len(set(got.tolist())) == topk
+        assert np.all(np.diff(got) > 0)
+        if topk:
+            assert got.min() >= vis_start and got.max() < vis_start + vis_len
+        s = min(sink, topk)
+        assert got[:s].tolist() == list(range(vis_start, vis_start + s))
+        if topk > s:
+            assert got[-1] == vis_start + vis_len - 1
+            assert np.all(np.diff(got[s:]) == 1)
+        # brute force: position p of the span is kept iff it is among the
+        # first s or the last topk - s positions
+        keep = [p for p in range(vis_start, vis_start + vis_len)
+                if p - vis_start < s or (vis_start + vis_len - 1 - p) < topk - s]
+        assert got.tolist() == keep
+
+
+def test_static_window_full_budget_is_the_span():
+    """K = vis_len keeps the whole span for any sink, so the draft over that
+    list is the dense model (the sparse == dense special case)."""
+    for sink in (0, 1, 7, 100):
+        assert oracle.static_window_idx(5, 40, sink, 40).tolist() == list(range(5, 45))
+
+
+def test_static_window_rejects():
+    for args in ((0, 10, 2, 11), (0, 10, -1, 3), (-1, 10, 2, 3), (0, 10, 2, -1)):
+        with pytest.raises(ValueError):
+            oracle.static_window_idx(*args)
