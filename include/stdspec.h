@@ -215,6 +215,32 @@ std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* shape, const voi
                                         size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * (b) without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the sparse draft call with its split-K partials in scratch
+ * memory the library owns, a static device array of
+ * STD_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends.  The call allocates and frees nothing.
+ *
+ * Arguments and result are those of std_sparse_decode_attn_dlen with
+ * len_dev_or_null given, else of std_sparse_decode_attn (length kv->len);
+ * the kernels and the split are the same, so the output equals theirs bit
+ * for bit.  The scratch needs no initialisation.
+ * Errors: every check of those calls; STD_ERR_WORKSPACE_TOO_SMALL when the
+ * partials would exceed the scratch (about 4 * n_q_heads * (head_dim + 2)
+ * bytes per 128 key-list entries; the 140k-context Qwen2-VL shape with
+ * K = 4,096 needs 0.7 MB), before any HIP call.
+ * Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ * that overlap on one GPU (different streams, or host threads) race; order
+ * them on one stream.
+ * ------------------------------------------------------------------------ */
+#define STD_NOALLOC_SCRATCH_BYTES (8u << 20)
+std_status_t std_sparse_decode_attn_noalloc(const std_attn_shape_t* shape, const void* q,
+                                            const std_kv_t* kv, const int32_t* len_dev_or_null,
+                                            int32_t len_offset, std_vis_t vis, const int32_t* idx,
+                                            int32_t topk, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * (b, batched) Sparse draft attention for `batch` independent sequences in
  * one launch: the draft step of (b) applied to each sequence, data-parallel
  * over requests (the pages fix no batch size; this serves batch > 1).

@@ -19,6 +19,8 @@ captured once and replayed; std_sparse_decode_attn_batch,
 std_dense_verify_attn_batch and std_accept_batch run the three decode steps
 for several independent sequences, one launch each (each sequence with its
 own valid length and, optionally, its own draft length).
+std_sparse_decode_attn_noalloc is the draft call for callers that cannot
+allocate: its partials live in scratch memory the library owns.
 std_static_window_idx writes the index lists of the streaming-attention
 comparator (attention sink + recent window over the visual span) for the
 same draft calls.  std_check_idx counts index-list entries that break the
@@ -35,6 +37,7 @@ from ._lib import (  # noqa: F401
     std_select_topk, std_select_topk_workspace,
     std_sparse_decode_attn, std_sparse_decode_workspace, std_sparse_decode_attn_dlen,
     std_sparse_decode_attn_batch, std_sparse_decode_batch_workspace,
+    std_sparse_decode_attn_noalloc,
     std_dense_verify_attn, std_dense_verify_workspace, std_dense_verify_attn_dlen,
     std_accept, std_accept_batch, std_dense_verify_attn_batch, std_dense_verify_batch_workspace,
     std_check_idx, std_hbm_read_probe, std_static_window_idx,

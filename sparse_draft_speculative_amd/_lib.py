@@ -64,6 +64,9 @@ _SIGS = {
                                                    _P, _SZ, _P]),
     "std_sparse_decode_attn": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, ctypes.POINTER(KV),
                                               Vis, _P, _I, _P, _P, _SZ, _P]),
+    "std_sparse_decode_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P,
+                                                      ctypes.POINTER(KV), _P, _I, Vis, _P, _I,
+                                                      _P, _P]),
     "std_sparse_decode_batch_workspace": (_SZ, [ctypes.POINTER(AttnShape), _I,
                                                 ctypes.POINTER(KV), Vis, _I]),
     "std_sparse_decode_attn_batch": (ctypes.c_int, [ctypes.POINTER(AttnShape), _P, _I,
@@ -455,6 +458,33 @@ def std_sparse_decode_attn_dlen(q, k, v, max_len, len_dev, len_offset, vis_start
                                            _ptr(len_dev), int(len_offset), vis, _ptr(idx), topk,
                                            _ptr(out), _ptr(ws), _ws_bytes(ws), _stream(stream)),
            "std_sparse_decode_attn_dlen")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def std_sparse_decode_attn_noalloc(q, k, v, length, vis_start, vis_len, idx, len_dev=None,
+                                   len_offset=0, out=None, scale=None, stream=None):
+    """Sparse draft attention with its partials in the library's own scratch
+    (no workspace; for callers that cannot allocate).  len_dev None: length
+    ``length``; else min(max(len_dev[0] + len_offset, lo), length) as in
+    std_sparse_decode_attn_dlen.  Calls overlapping on one GPU race."""
+    lib = load()
+    _check_len_dev(len_dev, 1)
+    _sparse_args(q, k, v, idx, out)
+    hq, d = q.shape
+    hkv = k.shape[0]
+    topk = idx.shape[1]
+    shape = attn_shape(hq, hkv, d, scale)
+    kv = kv_desc(k, v, length)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.std_sparse_decode_attn_noalloc(ctypes.byref(shape), _ptr(q), ctypes.byref(kv),
+                                              _ptr(len_dev), int(len_offset),
+                                              Vis(vis_start, vis_len), _ptr(idx), topk,
+                                              _ptr(out), _stream(stream)),
+           "std_sparse_decode_attn_noalloc")
     return out
 
 

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/stdspec.h"
 #include "internal.hpp"
 #include "prefill.hpp"
@@ -272,11 +274,11 @@ size_t std_sparse_decode_workspace(const std_attn_shape_t* s, const std_kv_t* kv
 
 namespace {
 
-std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t batch,
-                           const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
-                           std_vis_t vis, const int32_t* idx, int32_t topk,
-                           const int32_t* gamma_dev, int32_t step, void* out, void* ws,
-                           size_t ws_bytes, void* stream) {
+// Every host check of a sparse draft call except the workspace's.
+std_status_t check_sparse_args(const std_attn_shape_t* s, const void* q, int32_t batch,
+                               const std_kv_t* kv, std_vis_t vis, const int32_t* idx,
+                               int32_t topk, const int32_t* gamma_dev, int32_t step,
+                               const void* out) {
   TRY(check_sparse_call(s, kv, vis, topk, batch));
   CHECK(!gamma_dev || step >= 0, STD_ERR_INVALID_ARGUMENT, "need step (%d) >= 0", step);
   TRY(check_kv(kv, true));
@@ -284,6 +286,15 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t bat
   CHECK(topk == 0 || idx, STD_ERR_INVALID_ARGUMENT, "idx is null");
   CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
         STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
+  return ok();
+}
+
+std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t batch,
+                           const std_kv_t* kv, const int32_t* len_dev, int32_t len_off,
+                           std_vis_t vis, const int32_t* idx, int32_t topk,
+                           const int32_t* gamma_dev, int32_t step, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  TRY(check_sparse_args(s, q, batch, kv, vis, idx, topk, gamma_dev, step, out));
   const int splits = sparse_splits(kv, vis, topk);
   const SplitWorkspace w = split_workspace(splits, batch * s->n_q_heads, s->head_dim);
   TRY(check_ws(ws, ws_bytes, w.bytes()));
@@ -324,6 +335,62 @@ std_status_t std_sparse_decode_attn_dlen(const std_attn_shape_t* s, const void* 
   CHECK(len_dev, STD_ERR_INVALID_ARGUMENT, "len_dev is null");
   return sparse_decode(s, q, 1, kv, len_dev, len_offset, vis, idx, topk, nullptr, 0, out, ws,
                        ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- library-owned scratch
+// For std_sparse_decode_attn_noalloc (callers that cannot allocate).  Each
+// GPU the library runs on holds its own copy of this array until the process
+// ends.  On the host its name is only a stand-in, never a device address:
+// host code uses the address hipGetSymbolAddress returns, looked up once per
+// device with that device current and kept in g_scratch_ptr.
+namespace {
+
+__device__ __align__(256) uint8_t scratch[STD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+std_status_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  CHECK(dev >= 0 && dev < kMaxDevices, STD_ERR_UNSUPPORTED,
+        "device %d is past the library's scratch table (%d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    CHECK(p && ((uintptr_t)p & 255) == 0, STD_ERR_HIP, "scratch address not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+std_status_t std_sparse_decode_attn_noalloc(const std_attn_shape_t* s, const void* q,
+                                            const std_kv_t* kv, const int32_t* len_dev_or_null,
+                                            int32_t len_offset, std_vis_t vis,
+                                            const int32_t* idx, int32_t topk, void* out,
+                                            void* stream) {
+  // every argument check (the scratch size included) before the first HIP call
+  TRY(check_sparse_args(s, q, 1, kv, vis, idx, topk, nullptr, 0, out));
+  const size_t need =
+      split_workspace(sparse_splits(kv, vis, topk), s->n_q_heads, s->head_dim).bytes();
+  CHECK(need <= STD_NOALLOC_SCRATCH_BYTES, STD_ERR_WORKSPACE_TOO_SMALL,
+        "this call needs %zu bytes of scratch; the library holds %zu", need,
+        (size_t)STD_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  TRY(scratch_for_current_device(&ws));
+  return sparse_decode(s, q, 1, kv, len_dev_or_null, len_offset, vis, idx, topk, nullptr, 0, out,
+                       ws, STD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* s, int32_t batch,

@@ -437,3 +437,27 @@ def test_binding_rejects_bad_acceptance_buffers():
     _raises(lambda: _lib.std_static_window_idx(4, 0, 100, 8, 16,
                                                idx_out=torch.zeros(4, 15, dtype=torch.int32)),
             "idx_out must have shape")
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """The no-alloc draft call checks its arguments, the scratch size
+    included, before its first HIP call (so these run without a GPU)."""
+    lib = _lib.load()
+    sh = _shape()
+    P = ctypes.c_void_p
+    E = _lib.STD_ERR_INVALID_ARGUMENT
+
+    def call(kv=None, topk=64, q=FAKE, out=FAKE, vis=(0, 800)):
+        kv = kv or _kv()
+        return lib.std_sparse_decode_attn_noalloc(ctypes.byref(sh), P(q), ctypes.byref(kv), None,
+                                                  0, _lib.Vis(*vis), P(FAKE), topk, P(out), None)
+
+    assert call(topk=801) == E
+    assert call(q=0) == E
+    assert call(out=FAKE + 4) == E
+    assert call(kv=_kv(k=0)) == E
+    # a list of 2^20 visual entries needs 8,192 splits x 28 rows of partials
+    # (about 120 MB), past the library's 8 MiB
+    big = _kv(cap=(1 << 20) + 100, length=(1 << 20) + 50)
+    assert call(kv=big, topk=1 << 20, vis=(0, 1 << 20)) == _lib.STD_ERR_WORKSPACE_TOO_SMALL
+    assert b"scratch" in lib.std_last_error()
