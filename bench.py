@@ -465,6 +465,7 @@ def main():
     # measured HBM traffic comes from the committed counter summary while
     # the kernel source it was taken on is unchanged.
     dense_roof["traffic"] = recorded_traffic()
+    sparse_roof["traffic"] = recorded_traffic("sparse_traffic_bytes_per_launch")
     roofline = dense_roof
 
     line = {
@@ -819,7 +820,7 @@ def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
 STREAM_SINK = 64          # visual positions kept from the start in the static-set comparator
 
 TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "traffic_dense_verify_c4.md")
+                               "traffic_attention_c4.md")
 KERNEL_SOURCES = ["attention.hip", "tile.hpp", "common.hpp", "internal.hpp"]
 
 
@@ -840,9 +841,11 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per dense verify launch from the committed FETCH_SIZE /
-    WRITE_SIZE summary (copy-calibrated), or None when that summary is
+def recorded_traffic(key="traffic_bytes_per_launch"):
+    """HBM bytes per launch of a kernel from the committed FETCH_SIZE /
+    WRITE_SIZE summary (copy-calibrated): ``traffic_bytes_per_launch`` for
+    the dense verify call, ``sparse_traffic_bytes_per_launch`` for the
+    sparse draft call (main kernel + combine).  None when that summary is
     missing or was taken on different kernel sources."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
@@ -852,7 +855,7 @@ def recorded_traffic():
     if vals.get("kernel_source_sha256") != kernel_source_digest():
         return None
     try:
-        return int(vals["traffic_bytes_per_launch"])
+        return int(vals[key])
     except (KeyError, ValueError):
         return None
 
