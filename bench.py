@@ -714,6 +714,8 @@ def prefill_lse(lay, cfg):
 
 def cycle_stats(ms):
     """Median, p10 and p90 of the per-cycle times (draft + verify + accept)."""
+    if not ms:
+        return None
     q = lambda f: ms[min(len(ms) - 1, int(f * (len(ms) - 1) + 0.5))]  # noqa: E731
     return {"cycles": len(ms), "median": round(q(0.5), 4), "p10": round(q(0.1), 4),
             "p90": round(q(0.9), 4)}
