@@ -417,6 +417,10 @@ def main():
     batch_sparse = None if args.no_batch else batched_sparse(sd, cfg, layers[0], idx[0], st)
     batch_cycles = None if args.no_batch else batched_cycles(sd, cfg, layers, idx, st, pool,
                                                              args.batch_seqs)
+    # the same batch with a draft length of its own per sequence
+    mixed = [G - 2 * (b % 3) for b in range(args.batch_seqs)]
+    batch_mixed = None if args.no_batch else batched_cycles(sd, cfg, layers, idx, st, pool,
+                                                            args.batch_seqs, gammas=mixed)
 
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
@@ -507,6 +511,7 @@ def main():
         "prefill_then_selection": pf,
         "batched_sparse": batch_sparse,
         "batched_decode": batch_cycles,
+        "batched_decode_per_sequence_gamma": batch_mixed,
         "hbm_read_probe": probe,
         "projection": projection(cycle_ms, G, dense_ms_per_tok,
                                  L * attn_bytes_sparse(cfg, cfg.ctx + 1),
@@ -608,13 +613,16 @@ def batched_sparse(sd, cfg, lay, idx, st, batches=(1, 4, 16), reps=20):
     return out
 
 
-def batched_cycles(sd, cfg, layers, idx, st, pool, B, cycles=24):
+def batched_cycles(sd, cfg, layers, idx, st, pool, B, cycles=24, gammas=None):
     """Decode cycles for B sequences through the batched calls: per cycle
     gamma x 28 batched draft launches, 28 batched verify launches and one
     batched acceptance, captured as three graphs and replayed; every
     sequence keeps its own device length, advanced by its own n + 1.  The
     sequences are copies of the 28 c4 layers (distinct addresses), so the
-    bytes moved are B times a single sequence's."""
+    bytes moved are B times a single sequence's.  ``gammas`` (one per
+    sequence, each <= gamma) gives every sequence its own draft length:
+    draft step j runs only the sequences with j < gamma_b, the verify pass
+    takes 1 + gamma queries and each acceptance reads its own rows."""
     import torch
     G, L = cfg.gamma, len(layers)
     dev = layers[0]["k"].device
@@ -640,14 +648,17 @@ def batched_cycles(sd, cfg, layers, idx, st, pool, B, cycles=24):
     toks = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
     n_out = torch.zeros(B, dtype=torch.int32, device=dev)
     total = torch.zeros(B, dtype=torch.int32, device=dev)
+    gdev = None if gammas is None else torch.tensor(gammas, dtype=torch.int32, device=dev)
+    G_run = G if gammas is None else max(gammas)
     torch.cuda.synchronize()
 
     def draft_phase():
-        for j in range(G):
+        for j in range(G_run):
             for l in range(L):
                 sd.std_sparse_decode_attn_batch(qd[l][j], kb[l], vb[l], cap, cfg.vis_start,
                                                 cfg.vis_len, ib[l], len_dev=seq, len_offset=1 + j,
-                                                out=o_s, workspace=ws_s, stream=st)
+                                                gamma_dev=gdev, step=j, out=o_s, workspace=ws_s,
+                                                stream=st)
 
     def verify_phase():
         for l in range(L):
@@ -655,7 +666,8 @@ def batched_cycles(sd, cfg, layers, idx, st, pool, B, cycles=24):
                                            len_offset=G + 1, out=o_d, workspace=ws_d, stream=st)
 
     def accept():
-        sd.std_accept_batch(draft, logits, out_tokens=toks, n_out=n_out, seq_len=seq, stream=st)
+        sd.std_accept_batch(draft, logits, out_tokens=toks, n_out=n_out, seq_len=seq,
+                            gamma_dev=gdev, stream=st)
         total.add_(n_out)
 
     with torch.cuda.stream(st):
@@ -683,6 +695,7 @@ def batched_cycles(sd, cfg, layers, idx, st, pool, B, cycles=24):
     ms = e0.elapsed_time(e1)
     emitted = int(total.sum().item())
     out = {"sequences": B, "cycles": cycles, "ms_per_cycle": round(ms / cycles, 4),
+           "gammas": list(gammas) if gammas is not None else [G] * B,
            "tokens_emitted": emitted,
            "decode_tokens_per_s": round(emitted / (ms * 1e-3), 1),
            "note": "28 c4 layers per sequence, gamma draft steps + verify + acceptance per "
