@@ -257,3 +257,65 @@ def test_batched_cycle_per_sequence_gamma(lib):
         rows = gam[b] + 1
         ref = oracle.dense_verify(f64(qv[b][:rows]), f64(kb), f64(vb), ctx[b] + rows)
         assert np.max(np.abs(f64(verify[b][:rows]) - ref)) <= TOL, b
+
+
+def test_graph_replayed_batch_with_device_gammas(lib):
+    """One batched draft step and one batched acceptance captured once in a
+    HIP graph and replayed three times with the per-sequence draft lengths
+    changed on the device between replays (eager work and synchronisations
+    in between): every replay equals the eager calls with that replay's
+    lengths (draft outputs bit for bit, acceptance exactly)."""
+    import synth
+    B, hq, hkv, d, vis_len, topk, stride = 4, 28, 4, 128, 1500, 128, 5
+    ctx = (1700, 1601, 1800, 1650)
+    cap = max(ctx) + stride + 2
+    q, k, v, idx = make_batch(B, hq, hkv, d, 0, vis_len, cap, topk, seed=55)
+    cases = [synth.accept_case(stride, 1000, 0.7, seed=300 + b) for b in range(B)]
+    draft = torch.stack([c[0] for c in cases]).cuda()
+    logits = torch.stack([c[1] for c in cases]).contiguous().cuda()
+    seq = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    gdev = torch.zeros(B, dtype=torch.int32, device="cuda")
+    step = 1
+    out = torch.zeros_like(q)
+    toks = torch.empty(B, stride + 1, dtype=torch.int32, device="cuda")
+    n_out = torch.empty(B, dtype=torch.int32, device="cuda")
+    shape = lib.attn_shape(hq, hkv, d)
+    ws = torch.zeros(lib.std_sparse_decode_batch_workspace(shape, B, k, cap, 0, vis_len, topk),
+                     dtype=torch.uint8, device="cuda")
+    st = torch.cuda.Stream()
+    sp = lib.prepare_sparse_decode_batch(q, k, v, cap, 0, vis_len, idx, out, ws, len_dev=seq,
+                                         len_offset=1 + step, gamma_dev=gdev, step=step,
+                                         stream=st)
+    ac = lib.prepare_accept_batch(draft, logits, toks, n_out, gamma_dev=gdev, stream=st)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):          # warm-up outside the capture
+        sp()
+        ac()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        sp()
+        ac()
+    torch.cuda.synchronize()
+    for gam in ((5, 0, 3, 1), (2, 2, 2, 2), (0, 5, 1, 4)):
+        gdev.copy_(torch.tensor(gam, dtype=torch.int32))
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = torch.full_like(q, 3.0)
+        ref_out = lib.std_sparse_decode_attn_batch(q, k, v, cap, 0, vis_len, idx, len_dev=seq,
+                                                   len_offset=1 + step, gamma_dev=gdev,
+                                                   step=step, out=ref)
+        ref_t, ref_n = lib.std_accept_batch(draft, logits, gamma_dev=gdev)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), gam
+        for b in range(B):
+            if gam[b] <= step:
+                assert torch.equal(out[b], torch.full_like(q[b], 3.0)), (gam, b)
+        assert torch.equal(toks, ref_t) and torch.equal(n_out, ref_n), gam
+        for b in range(B):
+            want, want_n, _, _ = oracle.accept(cases[b][0][:gam[b]].numpy(),
+                                               f64(cases[b][1][:gam[b] + 1]))
+            assert int(n_out[b]) == want_n
+            assert toks[b][:gam[b] + 1].cpu().numpy().tolist() == want.tolist()

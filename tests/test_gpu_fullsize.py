@@ -228,3 +228,20 @@ def test_fullsize_140k_static_window_draft(lib, c4):
         err = max_abs(f64(out), ref)
         say(f"  static-window step {j} len={length}: max abs err {err:.3e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("layer", [13, 27])
+def test_fullsize_32k_other_layers_selection(lib, layer):
+    """Selection on two more layers of the 28-layer 32k workload, whose
+    planted fractions (drawn per layer from U[2 %, 10 %]) differ from layer
+    0's, against the oracle."""
+    cfg = synth.config("c3")
+    lay = synth.attention_layer(cfg, layer, device="cuda")
+    say(f"c3 layer {layer} selection")
+    idx, scores = lib.std_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
+                                      cfg.vis_start, cfg.vis_len, cfg.topk, want_scores=True)
+    torch.cuda.synchronize()
+    _, ref_scores = oracle.select_topk(f64(lay["q_text"]), f64(lay["k"]), cfg.text_start,
+                                       cfg.vis_start, cfg.vis_len, cfg.topk)
+    check_against_oracle(idx.cpu().numpy(), f64(scores), np.asarray(ref_scores), cfg.topk,
+                         cfg.vis_start)
