@@ -230,6 +230,8 @@ std_status_t std_dense_verify_attn_dlen(const std_attn_shape_t* shape, const voi
  * partials would exceed the scratch (about 4 * n_q_heads * (head_dim + 2)
  * bytes per 128 key-list entries; the 140k-context Qwen2-VL shape with
  * K = 4,096 needs 0.7 MB), before any HIP call.
+ * The call runs on the current device; a non-null stream must belong to it
+ * (STD_ERR_INVALID_ARGUMENT otherwise).
  * Concurrency: every call on one GPU shares that GPU's scratch, so calls
  * that overlap on one GPU (different streams, or host threads) race; order
  * them on one stream.

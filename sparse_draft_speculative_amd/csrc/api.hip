@@ -353,10 +353,20 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-std_status_t scratch_for_current_device(void** out) {
+// The scratch of the device the call's kernels run on: the current device,
+// which a non-null stream must belong to (the address of another device's
+// copy would be used on the wrong GPU).
+std_status_t scratch_for_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    CHECK(sdev == dev, STD_ERR_INVALID_ARGUMENT,
+          "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+  }
   CHECK(dev >= 0 && dev < kMaxDevices, STD_ERR_UNSUPPORTED,
         "device %d is past the library's scratch table (%d devices)", dev, kMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -388,7 +398,7 @@ std_status_t std_sparse_decode_attn_noalloc(const std_attn_shape_t* s, const voi
         "this call needs %zu bytes of scratch; the library holds %zu", need,
         (size_t)STD_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
-  TRY(scratch_for_current_device(&ws));
+  TRY(scratch_for_current_device(static_cast<hipStream_t>(stream), &ws));
   return sparse_decode(s, q, 1, kv, len_dev_or_null, len_offset, vis, idx, topk, nullptr, 0, out,
                        ws, STD_NOALLOC_SCRATCH_BYTES, stream);
 }
