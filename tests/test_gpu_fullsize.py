@@ -245,3 +245,36 @@ def test_fullsize_32k_other_layers_selection(lib, layer):
                                        cfg.vis_start, cfg.vis_len, cfg.topk)
     check_against_oracle(idx.cpu().numpy(), f64(scores), np.asarray(ref_scores), cfg.topk,
                          cfg.vis_start)
+
+
+@pytest.mark.timeout(1200)
+def test_fullsize_140k_batched_launches(lib, c4):
+    """The batched draft and verify launches at the full size, in the shape
+    the benchmark times (4 sequences of the 140k-context layer at distinct
+    addresses; with several sequences the verify's split count is raised to
+    fill whole rounds of the machine), each sequence at its own device
+    length, against the oracle."""
+    cfg, lay = c4["cfg"], c4["lay"]
+    B = 4
+    k = lay["k"][None].expand(B, *lay["k"].shape).contiguous()
+    v = lay["v"][None].expand(B, *lay["v"].shape).contiguous()
+    qd = lay["q_draft"][:B].contiguous()             # one draft query per sequence
+    qv = lay["q_verify"][None].expand(B, *lay["q_verify"].shape).contiguous()
+    idx = torch.from_numpy(np.asarray(c4["ref_idx"], dtype=np.int32)).cuda()
+    ib = idx[None].expand(B, *idx.shape).contiguous()
+    ctx = [cfg.ctx - 3 * b for b in range(B)]                 # per-sequence lengths
+    seq = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    out_d = lib.std_sparse_decode_attn_batch(qd, k, v, cfg.capacity, cfg.vis_start, cfg.vis_len,
+                                             ib, len_dev=seq, len_offset=1)
+    out_v = lib.std_dense_verify_attn_batch(qv, k, v, cfg.capacity, len_dev=seq,
+                                            len_offset=cfg.gamma + 1)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = oracle.sparse_decode(f64(qd[b]), c4["kf"], c4["vf"], ctx[b] + 1, cfg.vis_start,
+                                   cfg.vis_len, c4["ref_idx"])
+        e_d = max_abs(f64(out_d[b]), ref)
+        ref = oracle.dense_verify(f64(qv[b]), c4["kf"], c4["vf"], ctx[b] + cfg.gamma + 1)
+        e_v = max_abs(f64(out_v[b]), ref)
+        say(f"  sequence {b} length {ctx[b]}: draft err {e_d:.2e}, verify err {e_v:.2e}")
+        assert e_d <= TOL and e_v <= TOL
