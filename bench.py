@@ -470,6 +470,8 @@ def main():
     # the kernel source it was taken on is unchanged.
     dense_roof["traffic"] = recorded_traffic()
     sparse_roof["traffic"] = recorded_traffic("sparse_traffic_bytes_per_launch")
+    dense_roof["kernel_only"] = recorded_kernel_times("dense")
+    sparse_roof["kernel_only"] = recorded_kernel_times("sparse")
     roofline = dense_roof
 
     line = {
@@ -836,6 +838,8 @@ STREAM_SINK = 64          # visual positions kept from the start in the static-s
 
 TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "traffic_attention_c4.md")
+TRACE_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                             "kernel_trace_c4_request.md")
 KERNEL_SOURCES = ["attention.hip", "tile.hpp", "common.hpp", "internal.hpp"]
 
 
@@ -854,6 +858,25 @@ def kernel_source_digest():
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()
+
+
+def recorded_kernel_times(prefix):
+    """Kernel-only times of one attention call (main kernel, combine) in us
+    from the committed kernel-trace summary, or None when it is missing or
+    was taken on different kernel sources."""
+    try:
+        text = open(TRACE_SUMMARY).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^- (\w+): (\S+)$", text, flags=re.M))
+    if vals.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return {"main_kernel_us": float(vals[f"{prefix}_main_kernel_us"]),
+                "combine_us": float(vals[f"{prefix}_combine_us"]),
+                "source": "rocprofv3 kernel trace (profiles/kernel_trace_c4_request.md)"}
+    except (KeyError, ValueError):
+        return None
 
 
 def recorded_traffic(key="traffic_bytes_per_launch"):
