@@ -256,6 +256,7 @@ def main():
         torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    nvtx = torch.cuda.nvtx
 
     # n_out of each cycle lands in pinned host memory by an asynchronous copy
     # on the bench stream; the host reads it one cycle late (after launching
@@ -273,9 +274,12 @@ def main():
         cyc_ev = []
         inflight = []                      # (ring slot, copy-done event)
         with torch.cuda.stream(st):
+            # host-side ranges (roctx through torch.cuda.nvtx) for a marker trace
+            nvtx.range_push("selection")
             e_sel[0].record()
             select_all()
             e_sel[1].record()
+            nvtx.range_pop()
             seq.fill_(cfg.ctx)
             t = cfg.ctx
             produced = 1                   # the pending token x_t comes from prefill
@@ -287,12 +291,18 @@ def main():
                         and len(inflight) < RING):
                     es = (ev(), ev(), ev(), ev())
                     es[0].record()
+                    nvtx.range_push("draft")
                     run_draft()
                     es[1].record()
+                    nvtx.range_pop()
+                    nvtx.range_push("verify")
                     run_verify()
                     es[2].record()
+                    nvtx.range_pop()
+                    nvtx.range_push("accept")
                     run_accept[cycles % len(run_accept)]()
                     es[3].record()
+                    nvtx.range_pop()
                     cyc_ev.append(es)
                     slot = cycles % RING
                     n_host[slot:slot + 1].copy_(n_out, non_blocking=True)

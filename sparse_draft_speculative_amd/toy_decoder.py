@@ -244,17 +244,24 @@ class ToyDecoder:
         out_tokens = torch.empty(gamma + 1, dtype=torch.int32, device=self.dev)
         n_out = torch.empty(1, dtype=torch.int32, device=self.dev)
         sparse = (idx, vis_start, vis_len)
+        nvtx = torch.cuda.nvtx                           # roctx ranges for a marker trace
         while len(out) < n_new:
             if t + gamma + 1 > self.capacity:
                 raise ValueError("decoding ran past the cache capacity")
             tok = x_t
+            nvtx.range_push("draft")
             for j in range(gamma):                      # sparse model drafts
                 logits = self.forward(self.embed[tok.long()], t + j, sparse=sparse)
                 tok = self.argmax(logits)
                 draft[j:j + 1] = tok
+            nvtx.range_pop()
+            nvtx.range_push("verify")
             seq = torch.cat([x_t, draft])               # dense model verifies
             logits = self.forward(self.embed[seq.long()], t)
+            nvtx.range_pop()
+            nvtx.range_push("accept")
             _lib.std_accept(draft, logits, out_tokens=out_tokens, n_out=n_out)
+            nvtx.range_pop()
             n = int(n_out.item())
             emitted = out_tokens[:n].tolist()
             accepted.append(n - 1)

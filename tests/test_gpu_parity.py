@@ -380,3 +380,29 @@ def test_sparse_decode_clamps_out_of_span_positions(lib, name):
             ref_raw[h] = oracle.attend(qf[h], kf[g, keys], vf[g, keys], scale)
     assert max_abs(ref, ref_raw) > 2 * TOL[cfg.dtype]      # the case discriminates
     assert max_abs(out, ref) <= TOL[cfg.dtype]
+
+
+def test_every_call_is_bitwise_repeatable(lib):
+    """No reduction in the library uses floating-point atomics and every
+    merge has a fixed order, so running a call twice on the same inputs
+    gives the same bits: selection (scores and positions), the sparse draft
+    call, the prefill text attention (output and normalisers) and the
+    acceptance (tokens, count, margins)."""
+    cfg = synth.config("c2")
+    lay = layer(cfg)
+    runs = []
+    for _ in range(2):
+        idx, sc = lib.std_select_topk(lay["q_text"], lay["k"], cfg.ctx, cfg.text_start,
+                                      cfg.vis_start, cfg.vis_len, cfg.topk, want_scores=True)
+        sp = lib.std_sparse_decode_attn(lay["q_draft"][0].contiguous(), lay["k"], lay["v"],
+                                        cfg.draft_len(0), cfg.vis_start, cfg.vis_len, idx)
+        pf, lse = lib.std_prefill_text_attn(lay["q_text"], lay["k"], lay["v"], cfg.ctx,
+                                            cfg.text_start)
+        draft, logits = synth.accept_case(cfg.gamma, 4096, 0.8, seed=9, dtype=torch.bfloat16,
+                                          n_ties=1)
+        margins = torch.empty(cfg.gamma + 1, dtype=torch.float32, device="cuda")
+        toks, n_out = lib.std_accept(draft.cuda(), logits.cuda(), margins=margins)
+        torch.cuda.synchronize()
+        runs.append([idx, sc, sp, pf, lse, toks, n_out, margins])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
