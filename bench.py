@@ -81,6 +81,11 @@ def parse():
     return ap.parse_args()
 
 
+def say(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(msg, file=sys.stderr, flush=True)
+
+
 def attn_bytes_dense(cfg, length, n_q):
     e = 2
     return 2 * cfg.n_kv_heads * length * cfg.head_dim * e + 2 * n_q * cfg.n_q_heads * cfg.head_dim * e
@@ -333,6 +338,7 @@ def main():
                   "sparse_bytes": sp_bytes, "dense_bytes": dv_bytes, "emitted": emitted}
         return min(produced, args.new_tokens), cycles, ph
 
+    say("# timing the requests")
     for _ in range(args.warmup):
         run_request(False)
     torch.cuda.synchronize()
@@ -350,6 +356,7 @@ def main():
     # selection with the row normaliser (step 1) supplied by the caller, as
     # a prefill attention kernel returns it; the LSE itself is computed here
     # in fp32 torch, outside the timed region
+    say(f"# requests done: {new_tok / wall:.1f} tokens/s; selection with a caller LSE")
     sel_prefill = None
     if not args.no_prefill_lse:
         lses = [prefill_lse(lay, cfg) for lay in layers]
@@ -378,6 +385,7 @@ def main():
     # Selection beside the prefill: the text rows' prefill attention returns
     # their normalisers (std_prefill_text_attn) and the selection takes
     # those instead of computing its first pass
+    say("# prefill text attention, then selection on its normalisers")
     pf = None
     if not args.no_prefill:
         pf_ws = torch.zeros(max(sd.std_prefill_text_attn_workspace(shape, cfg.text_start,
@@ -424,6 +432,7 @@ def main():
                       "their causal keys, 28 layers), then the 28 selections fed those "
                       "normalisers"}
 
+    say("# batched launches")
     batch_sparse = None if args.no_batch else batched_sparse(sd, cfg, layers[0], idx[0], st)
     batch_cycles = None if args.no_batch else batched_cycles(sd, cfg, layers, idx, st, pool,
                                                              args.batch_seqs)
@@ -432,6 +441,7 @@ def main():
     batch_mixed = None if args.no_batch else batched_cycles(sd, cfg, layers, idx, st, pool,
                                                             args.batch_seqs, gammas=mixed)
 
+    say("# dense-only decoding and the read probe")
     # dense-only decoding baseline: 28 dense n_q=1 calls per token
     torch.cuda.synchronize()
     e0, e1 = ev(), ev()
@@ -531,8 +541,10 @@ def main():
                                  L * attn_bytes_dense(cfg, cfg.ctx + 1, 1)),
     }
     if not args.no_toy:
+        say("# toy decoder end to end")
         line["toy_e2e"] = toy_e2e()
     if not args.no_cpu_baseline:
+        say("# oracle on the host (bounded sample)")
         line["cpu_baseline"] = cpu_baseline(cfg, cpu_layers, args, cycles / args.steps)
     print(json.dumps(line), flush=True)
 
