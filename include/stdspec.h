@@ -21,7 +21,9 @@
  *   shape structs are HOST pointers read during the call only.  The caller
  *   owns every buffer.  The library allocates and frees nothing and keeps no
  *   state between calls, so calls on different streams do not interfere
- *   (except through buffers the caller shares between them).
+ *   (except through buffers the caller shares between them).  The one
+ *   exception is std_sparse_decode_attn_noalloc, whose partials live in a
+ *   static device array the library holds per GPU (see there).
  * - KV cache of one layer: separate K and V, each [n_kv_heads][capacity]
  *   [head_dim], row-major, dtype bf16 or fp32; positions [0, len) are valid.
  * - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
