@@ -67,5 +67,26 @@ def build(verbose=False):
     return LIB
 
 
+TEST_PROGRAM_SRC = os.path.join(ROOT, "tests", "cycle_from_c.hip")
+TEST_PROGRAM = os.path.join(ROOT, "tests", "_build", "cycle_from_c")
+
+
+def build_test_program(verbose=False):
+    """The GPU test program that drives a cycle through the C ABI alone
+    (tests/cycle_from_c.hip), linked against the in-tree libstdspec.so."""
+    os.makedirs(os.path.dirname(TEST_PROGRAM), exist_ok=True)
+    cmd = [hipcc(), *FLAGS, TEST_PROGRAM_SRC, "-L", HERE, "-lstdspec",
+           "-Wl,-rpath,$ORIGIN/../../sparse_draft_speculative_amd", "-o", TEST_PROGRAM]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if res.returncode != 0:
+        out = res.stdout.decode(errors="replace")
+        print("\n".join(ln for ln in out.splitlines() if "packed-fp32-ops" not in ln),
+              file=sys.stderr)
+        raise RuntimeError("hipcc failed for tests/cycle_from_c.hip")
+    return TEST_PROGRAM
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
