@@ -524,6 +524,11 @@ def main():
         "attn_mb_per_emitted_token": round((ph["sparse_bytes"] + ph["dense_bytes"])
                                            / max(ph["emitted"], 1) / 1e6, 1),
         "dense_only_tokens_per_s": round(1e3 / dense_ms_per_tok, 2),
+        # emitted tokens over the event-timed decode cycles alone: the selection
+        # (once per request, at prefill) and the host gaps between cycles are out
+        "decode_tokens_per_s": round(ph["emitted"] / (sum(cycle_ms) * 1e-3), 2),
+        "decode_speedup_vs_dense_only": round(ph["emitted"] / (sum(cycle_ms) * 1e-3)
+                                              * dense_ms_per_tok / 1e3, 3),
         "dense_only_attn_gbps": round(dense_gbps, 1),
         "cycle_ms": cycle_stats(cycle_ms),
         "inter_cycle_gap_ms": cycle_stats(gap_ms),
