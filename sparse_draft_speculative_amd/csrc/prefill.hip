@@ -8,15 +8,20 @@
 // row i, and lse = log of that softmax's denominator, which the selection
 // call accepts in place of computing it.
 //
-//  prefill_mfma_kernel -- one workgroup = 16 waves x 16 rows = 256 rows of
+//  prefill_mfma_kernel -- one workgroup = 8 waves x 32 rows = 256 rows of
 //      one KV head group (the G heads' rows stacked, as the selection
-//      kernels lay them out) against one chunk of kPfChunk keys, four waves
-//      per SIMD.  Q stays in registers; K and V tiles of 64 keys move
+//      kernels lay them out) against one chunk of kPfChunk keys, two waves
+//      per SIMD.  Each wave holds two 16-row blocks, so every K and V
+//      fragment it reads from LDS feeds two MFMAs (LDS reads are half of
+//      what one block per wave at four waves per SIMD needs; that form ran
+//      9 % slower).  Q stays in registers; K and V tiles of 64 keys move
 //      global -> LDS by direct-to-LDS copies (four buffers, three tiles in
-//      flight).  Per tile: S^T = K Q^T on the matrix unit, the row's running
-//      max (shared by the row's four lanes), P = 2^(s c - m), O^T += V^T P^T
-//      on the matrix unit with V^T taken by transpose reads.  The chunk's
-//      (m, l, O) per row go to the workspace.
+//      flight).  Per tile: S^T = K Q^T on the matrix unit, P = 2^(s c - m)
+//      against the row's lazy running max (shared by the row's four lanes;
+//      it moves only when a score passes it by 2^8, found from the P sums,
+//      so the per-score max is off the common path), O^T += V^T P^T on the
+//      matrix unit with V^T taken by transpose reads.  The chunk's (m, l, O)
+//      per row go to the workspace.
 //  prefill_merge -- one wave per row: merges the chunks into O (bf16) and
 //      the natural-log normaliser.
 
@@ -28,9 +33,9 @@
 namespace stdspec {
 namespace {
 
-constexpr int kPfWaves = 16;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfRB = 1;                                  // 16-row blocks per wave
+constexpr int kPfRB = 2;                                  // 16-row blocks per wave
 constexpr int kPfRowsWg = kPfWaves * 16 * kPfRB;          // rows per workgroup
 constexpr int kPfOcc = kPfWaves / 4;                      // waves per SIMD
 constexpr int kPfBufs = 4;                                // tile buffers (a power of two)
@@ -50,6 +55,74 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 __device__ __forceinline__ int pf_item(int bid, int n_items) {
   const int per = (n_items + kPfXcds - 1) / kPfXcds;
   return (bid % kPfXcds) * per + bid / kPfXcds;
+}
+
+// S^T = K Q^T for one 64-key tile: s[r][kb] holds keys 16 kb + 4 grp + i
+// of the tile for row col of block r.  The K fragments of two key blocks
+// are read before their MFMAs.
+template <int D>
+__device__ __forceinline__ void pf_scores(const uint16_t* Ks, const bf16x8_t (*qb)[D / 32],
+                                          int col, int grp, floatx4_t (&s)[kPfRB][4]) {
+  constexpr int KST = D / 32;
+#pragma unroll
+  for (int kp = 0; kp < 4; kp += 2) {
+    u32x4_t a[2][KST];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk)
+        a[b2][kk] = *reinterpret_cast<const u32x4_t*>(
+            Ks + Tile<D>::off_k((kp + b2) * 16 + col, KST * grp + kk));
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < kPfRB; ++r) s[r][kp + b2] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < kPfRB; ++r)
+          s[r][kp + b2] = mfma_bf16(as_bf16x8(a[b2][kk]), qb[r][kk], s[r][kp + b2]);
+  }
+}
+
+// The same scores with one key block's K fragments in registers at a time
+// (fewer registers, for the rare slow path).
+template <int D>
+__device__ __forceinline__ void pf_scores_lean(const uint16_t* Ks, const bf16x8_t (*qb)[D / 32],
+                                               int col, int grp, floatx4_t (&s)[kPfRB][4]) {
+  constexpr int KST = D / 32;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int r = 0; r < kPfRB; ++r) s[r][kb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+          Ks + Tile<D>::off_k(kb * 16 + col, KST * grp + kk));
+#pragma unroll
+      for (int r = 0; r < kPfRB; ++r) s[r][kb] = mfma_bf16(as_bf16x8(a), qb[r][kk], s[r][kb]);
+    }
+    // keeps the scheduler from hoisting every block's fragment reads
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Keys at or past the chunk end, or after the row's own position, score
+// -inf (selects only: the compares are per lane).
+__device__ __forceinline__ void pf_mask(floatx4_t (&s)[kPfRB][4], int t0, int grp, int key1,
+                                        const int (&rpos)[kPfRB]) {
+#pragma unroll
+  for (int r = 0; r < kPfRB; ++r)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = t0 + kb * 16 + 4 * grp + i;
+        const bool vis = (key < key1) & (key <= rpos[r]);
+        s[r][kb][i] = vis ? s[r][kb][i] : -INFINITY;
+      }
 }
 
 template <int D>
@@ -153,67 +226,70 @@ __global__ __launch_bounds__(kPfThreads, kPfOcc) void prefill_mfma_kernel(
     const uint16_t* Ks = smem + (t & (NB - 1)) * 2 * TILE;
     const uint16_t* Vs = Ks + TILE;
     const int t0 = key0 + t * 64;
-    // keys at or before text_start are visible to every text row
+    // keys at or before text_start are visible to every text row (wave-uniform)
     const bool interior = t0 + 64 <= key1 && t0 + 63 <= text_start;
 
-    // S^T = K Q^T: lane (col, grp) gets keys t0 + kb*16 + 4 grp + i of row
-    // col; the K fragments of two key blocks are read before their MFMAs
-    floatx4_t sacc[kPfRB][4];
+    // Fast path: the probabilities against the running max as it stands,
+    // P = 2^(s c - m), computed in place of the scores.  While no score of
+    // the tile exceeds the max by 2^8 each P is at most 2^8, so a lane sum
+    // above 2^8 (or NaN / inf: the max is still unset) flags a row whose max
+    // may have to move; then the whole wave (the MFMAs cover every lane)
+    // recomputes the tile's scores and applies the max rule row by row.
+    // Rows whose max stays get the same P either way.
+    floatx4_t sp[kPfRB][4];
+    pf_scores<D>(Ks, qb, col, grp, sp);
+    if (!interior) pf_mask(sp, t0, grp, key1, rpos);
+    float ts[kPfRB];
+    bool ok = true;
 #pragma unroll
-    for (int kp = 0; kp < 4; kp += 2) {
-      u32x4_t a[2][KST];
+    for (int r = 0; r < kPfRB; ++r) {
+      ts[r] = 0.f;
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < KST; ++kk)
-          a[b2][kk] = *reinterpret_cast<const u32x4_t*>(
-              Ks + Tile<D>::off_k((kp + b2) * 16 + col, KST * grp + kk));
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < kPfRB; ++r) sacc[r][kp + b2] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KST; ++kk)
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int r = 0; r < kPfRB; ++r)
-            sacc[r][kp + b2] = mfma_bf16(as_bf16x8(a[b2][kk]), qb[r][kk], sacc[r][kp + b2]);
+        for (int i = 0; i < 4; ++i) {
+          sp[r][kb][i] = fast_exp2(fmaf(sp[r][kb][i], c, -m[r]));
+          ts[r] += sp[r][kb][i];
+        }
+      ok = ok && ts[r] <= 256.f;
     }
-
-    // mask, running max per row on the raw scores (c > 0; the row's four
-    // lanes agree), P = 2^(s c - m) with the scale folded into one FMA
+    if (__any(!ok)) {                     // wave-uniform; the first tile of a chunk, then rare
+      pf_scores_lean<D>(Ks, qb, col, grp, sp);
+      if (!interior) pf_mask(sp, t0, grp, key1, rpos);
+#pragma unroll
+      for (int r = 0; r < kPfRB; ++r) {
+        // the row's max on the raw scores (c > 0; the row's four lanes agree)
+        float tmax = sp[r][0][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sp[r][kb][i]);
+        tmax = max_over_groups(tmax) * c;
+        if (tmax > m[r] + 8.f) {          // also while m = -inf
+          const float alpha = (m[r] == -INFINITY) ? 0.f : fast_exp2(m[r] - tmax);
+          l[r] *= (double)alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[r][db] *= alpha;
+          m[r] = tmax;
+        }
+        const float nms = (m[r] == -INFINITY) ? 0.f : -m[r];
+        ts[r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sp[r][kb][i] = fast_exp2(fmaf(sp[r][kb][i], c, nms));
+            ts[r] += sp[r][kb][i];
+          }
+      }
+    }
     uint32_t pw[kPfRB][8];
 #pragma unroll
     for (int r = 0; r < kPfRB; ++r) {
-      float x[16];
+      l[r] += (double)ts[r];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = t0 + (j >> 2) * 16 + 4 * grp + (j & 3);
-        x[j] = (interior || (key < key1 && key <= rpos[r])) ? sacc[r][j >> 2][j & 3] : -INFINITY;
-      }
-      float tmax = x[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
-      tmax = max_over_groups(tmax) * c;
-      if (tmax > m[r] + 8.f) {            // rare after the first tile; also while m = -inf
-        const float alpha = (m[r] == -INFINITY) ? 0.f : fast_exp2(m[r] - tmax);
-        l[r] *= (double)alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[r][db] *= alpha;
-        m[r] = tmax;
-      }
-      const float nms = (m[r] == -INFINITY) ? 0.f : -m[r];
-      float pj[16];
-      float ts = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        pj[j] = fast_exp2(fmaf(x[j], c, nms));
-        ts += pj[j];
-      }
-      l[r] += (double)ts;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) pw[r][w] = pack2_bf16(pj[2 * w], pj[2 * w + 1]);
+      for (int w = 0; w < 8; ++w)
+        pw[r][w] = pack2_bf16(sp[r][w >> 1][2 * (w & 1)], sp[r][w >> 1][2 * (w & 1) + 1]);
     }
 
     // O^T += V^T P^T in two 32-key steps.  The B operand holds the lane's
