@@ -130,3 +130,44 @@ def test_prefill_lse_drives_the_selection(lib):
         assert len(sel) == cfg.topk
         bad = [j for j in ref ^ sel if abs(s[j] - kth) > 1e-6 * kth]
         assert not bad, f"head {g}: {bad[:5]}"
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_running_max_moves_inside_a_chunk(lib, d):
+    """Keys whose scores climb by more than 2^8 (in base 2) at points inside
+    both key chunks move every row's running max mid-chunk, and each move
+    rescales what the row has summed so far; the normaliser exposes a
+    missed or wrong rescale.  Text queries share a direction u; planted keys
+    a*u with growing a sit inside tiles (none at a tile start).  The
+    normaliser reaches 25-45 here, so its bar is the same 2e-6 relative that
+    TOL_LSE is at O(10)."""
+    hq, hkv, text_start, n_text = 8, 2, 20000, 50
+    gen = torch.Generator(device="cpu").manual_seed(2024 + d)
+    cap = text_start + n_text + 3
+    u = torch.randn(d, generator=gen)
+    u = u / u.norm()
+    k = torch.randn(hkv, cap, d, generator=gen)
+    v = torch.randn(hkv, cap, d, generator=gen)
+    q = 0.3 * torch.randn(hq, n_text, d, generator=gen) + 4.0 * u
+    # q.u lies in about [3.1, 4.9], so in base-2 units (scale log2 e / sqrt(d))
+    # each planted key clears the previous maximum by at least 8.8 here
+    scale2 = 1.4426950408889634 / d ** 0.5
+    step, a0 = 9.0 / (scale2 * 3.1), 11.5 / (scale2 * 3.1)
+    plant = [700, 5003, 9999, 17011]
+    for n, pos in enumerate(plant):
+        k[:, pos] = (a0 + n * step) * u
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    say(f"prefill max moves d={d} planted at {plant}")
+    length = text_start + n_text
+    out, lse = lib.std_prefill_text_attn(q.cuda(), k.cuda(), v.cuda(), length, text_start)
+    torch.cuda.synchronize()
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    # every row's scores climb past its running max at each planted key
+    G = hq // hkv
+    s = np.einsum("hid,hkd->hik", qf, np.repeat(kf, G, axis=0)) * scale2
+    seq = [s[:, :, :plant[0]].max(axis=2)] + [s[:, :, p] for p in plant]
+    assert min(float(np.min(b - a)) for a, b in zip(seq, seq[1:])) > 8.0
+    ref = oracle.dense_verify(qf.transpose(1, 0, 2), kf, vf, length).transpose(1, 0, 2)
+    ref_lse = oracle.row_lse(qf.transpose(1, 0, 2), kf, length).T
+    assert np.max(np.abs(f64(out) - ref)) <= TOL_OUT
+    assert np.max(np.abs(f64(lse) - ref_lse) / np.maximum(np.abs(ref_lse), 10.0)) <= TOL_LSE / 10
