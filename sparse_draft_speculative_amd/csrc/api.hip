@@ -101,19 +101,24 @@ int sparse_splits(const std_kv_t* kv, std_vis_t vis, int topk) {
   return (L + kSparseChunk - 1) / kSparseChunk;
 }
 
-// One sequence: dense_split_count.  A batch of several runs in rounds of
-// 256 workgroups (one per CU), so its split count is raised until the grid
-// fills whole rounds (the row blocks of a sequence count once here: at the
-// verify shapes a sequence has one).
-int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int* chunk, int batch = 1) {
+// One sequence: dense_split_count.  A batch of several sequences runs in
+// rounds of 256 workgroups (one per CU).  Measured at 140k keys, 2 to 16
+// sequences: whole rounds and long workgroups read fastest (6.1-6.5 TB/s,
+// against 5.2-5.6 with the split count of one sequence rounded up to
+// whole rounds), so the split count fills one round, or two when every
+// workgroup then still streams at least 128 tiles of 64 keys.
+int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int n_q, int* chunk,
+                 int batch = 1) {
   *chunk = 64;                                   // tile size; splits interleave tiles
-  const int S = dense_split_count(kv->len, s->n_kv_heads);
-  if (batch <= 1) return S;
-  const long long per_round = 256, wg = (long long)batch * s->n_kv_heads;
-  const long long rounds = (wg * S + per_round - 1) / per_round;
-  const long long full = (rounds * per_round) / wg;
-  const int tiles = (kv->len + 63) / 64;
-  return (int)(full < tiles ? (full > S ? full : S) : tiles);
+  if (batch <= 1) return dense_split_count(kv->len, s->n_kv_heads);
+  const long long tiles = (kv->len + 63) / 64;
+  const long long row_blocks = ((long long)n_q * (s->n_q_heads / s->n_kv_heads) + 63) / 64;
+  const long long wg = (long long)batch * s->n_kv_heads * row_blocks;   // per split
+  const long long rounds = tiles * wg >= 128LL * 512 ? 2 : 1;
+  long long S = 256 * rounds / wg;
+  if (S < 1) S = 1;
+  if (S > tiles) S = tiles;
+  return (int)S;
 }
 
 std_status_t check_ws(void* ws, size_t have, size_t need) {
@@ -196,7 +201,7 @@ const char* std_last_error(void) { return g_err; }
 size_t std_dense_verify_workspace(const std_attn_shape_t* s, int32_t n_q, const std_kv_t* kv) {
   if (check_dense(s, kv, n_q, 1) != STD_OK) return 0;
   int chunk;
-  const int splits = dense_splits(s, kv, &chunk);
+  const int splits = dense_splits(s, kv, n_q, &chunk);
   return split_workspace(splits, n_q * s->n_q_heads, s->head_dim).bytes();
 }
 
@@ -213,7 +218,7 @@ std_status_t dense_verify(const std_attn_shape_t* s, const void* q, int32_t n_q,
   CHECK(aligned16(q) && aligned16(kv->k) && aligned16(kv->v) && aligned16(out),
         STD_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned");
   int chunk;
-  const int splits = dense_splits(s, kv, &chunk, batch);
+  const int splits = dense_splits(s, kv, n_q, &chunk, batch);
   const SplitWorkspace w = split_workspace(splits, batch * n_q * s->n_q_heads, s->head_dim);
   TRY(check_ws(ws, ws_bytes, w.bytes()));
   AttnArgs a{};
@@ -252,7 +257,7 @@ size_t std_dense_verify_batch_workspace(const std_attn_shape_t* s, int32_t n_q, 
                                         const std_kv_t* kv) {
   if (check_dense(s, kv, n_q, batch) != STD_OK) return 0;
   int chunk;
-  const int splits = dense_splits(s, kv, &chunk, batch);
+  const int splits = dense_splits(s, kv, n_q, &chunk, batch);
   return split_workspace(splits, batch * n_q * s->n_q_heads, s->head_dim).bytes();
 }
 
