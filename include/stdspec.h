@@ -295,8 +295,9 @@ std_status_t std_sparse_decode_attn_batch(const std_attn_shape_t* shape, const v
  * them change nothing in them) and std_accept_batch reads only those.
  * bf16 only for batch > 1 (fp32: STD_ERR_UNSUPPORTED); batch = 1 is
  * std_dense_verify_attn(_dlen) bit for bit.  With batch > 1 the key split
- * count is raised so the grid fills whole rounds of the machine, which can
- * change the summation order (results stay within the same tolerance).
+ * count is chosen so the grid fills one whole round of the machine (two
+ * when each workgroup still streams at least 128 tiles of 64 keys), which
+ * changes the summation order (results stay within the same tolerance).
  * ------------------------------------------------------------------------ */
 size_t std_dense_verify_batch_workspace(const std_attn_shape_t* shape, int32_t n_q,
                                         int32_t batch, const std_kv_t* kv);
@@ -324,6 +325,8 @@ std_status_t std_dense_verify_attn_batch(const std_attn_shape_t* shape, const vo
  * n_out        int32 device scalar: n + 1, in [1, gamma + 1].
  * margins_or_null  [gamma+1] fp32 device: top1 - top2 of each row (0 on a
  *              tie at the top).
+ * Logits are expected finite: a row holding a NaN gets an unspecified
+ * prediction and margin (no error is raised).
  * seq_len_inout_or_null  int32 device scalar; if given, n + 1 is added.
  * ------------------------------------------------------------------------ */
 std_status_t std_accept(const int32_t* draft, int32_t gamma, const void* logits,
