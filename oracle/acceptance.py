@@ -30,7 +30,8 @@ def argmax_margin(row):
     if row.size == 1:
         return best, np.inf
     rest = np.delete(row, best)
-    return best, float(row[best] - rest.max())
+    with np.errstate(invalid="ignore"):        # a row of -inf: the margin is NaN
+        return best, float(row[best] - rest.max())
 
 
 def accept(draft, logits):

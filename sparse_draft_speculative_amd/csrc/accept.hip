@@ -41,15 +41,37 @@ __device__ __forceinline__ int seq_gamma(const int32_t* gamma_dev, int b, int ga
   return gamma_dev ? min(max(gamma_dev[b], 0), gamma) : gamma;
 }
 
+// Elements reach a thread in increasing id order, so only a strictly larger
+// value takes over (the first maximum wins); the runner-up is the larger of
+// the old runner-up and the smaller of (best, x).
 __device__ __forceinline__ void consider(Best& b, float x, int j) {
-  // elements reach a thread in increasing id order: the first maximum wins
-  if (x > b.v || b.i == 0x7fffffff) { b.v2 = fmaxf(b.v2, b.v); b.v = x; b.i = j; }
-  else b.v2 = fmaxf(b.v2, x);
+  b.i = x > b.v ? j : b.i;
+  b.v2 = fmaxf(b.v2, fminf(b.v, x));
+  b.v = fmaxf(b.v, x);
+}
+
+// The ids of one 16-byte chunk of a row as fp32 values.
+template <typename T>
+__device__ __forceinline__ void chunk_values(const uint4& u, float (&x)[16 / sizeof(T)]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      x[e] = __uint_as_float((e & 1) ? (w[e / 2] & 0xffff0000u) : (w[e / 2] << 16));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+  }
 }
 
 // One workgroup per logit row.  Rows whose length is a multiple of 8 are read
-// with 16-byte loads (8 ids per thread per step), others element by element.
-template <typename T>
+// with 16-byte loads (8 bf16 or 4 fp32 ids per thread per step), others
+// element by element.  On the 16-byte path a thread keeps its best value and
+// the first chunk that holds it (a chunk takes over only with a strictly
+// larger maximum, so the earliest chunk wins ties); the id inside that chunk
+// is found once at the end by reading the chunk again.  The runner-up value
+// is tracked element by element only when margins are asked for.
+template <typename T, bool MARGIN>
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T* __restrict__ logits,
                                                               int vocab, int gamma,
                                                               const int32_t* __restrict__ gamma_dev,
@@ -61,31 +83,48 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T* __restric
   if (gamma_dev && row % (gamma + 1) > seq_gamma(gamma_dev, row / (gamma + 1), gamma)) {
     if (tid == 0) {
       pred[row] = -1;
-      if (margins) margins[row] = __builtin_nanf("");
+      if (MARGIN) margins[row] = __builtin_nanf("");
     }
     return;
   }
   const T* lr = logits + (size_t)row * vocab;
-  Best b{-INFINITY, 0x7fffffff, -INFINITY};
   constexpr int kVec = 16 / sizeof(T);                 // ids per 16-byte load
   const bool vec = (vocab % 8) == 0 && (reinterpret_cast<uintptr_t>(lr) & 15) == 0;
+  // a thread that sees no id keeps the sentinel id and -inf, which loses
+  // every merge against a thread that saw one
+  Best b{-INFINITY, 0x7fffffff, -INFINITY};
   if (vec) {
     const int nchunk = vocab / kVec;
+    int cb = tid < nchunk ? tid : -1;                  // chunk holding the best so far
 #pragma unroll 4
     for (int c = tid; c < nchunk; c += kArgmaxThreads) {
-      const uint4 u = *reinterpret_cast<const uint4*>(lr + (size_t)c * kVec);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-      if constexpr (sizeof(T) == 2) {
+      float x[kVec];
+      chunk_values<T>(*reinterpret_cast<const uint4*>(lr + (size_t)c * kVec), x);
+      float m = x[0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          consider(b, bf16_bits_to_f32((w[e / 2] >> (16 * (e & 1))) & 0xffffu), c * 8 + e);
-      } else {
+      for (int e = 1; e < kVec; ++e) m = fmaxf(m, x[e]);
+      if constexpr (MARGIN) {
+        float v = b.v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) consider(b, __uint_as_float(w[e]), c * 4 + e);
+        for (int e = 0; e < kVec; ++e) {
+          b.v2 = fmaxf(b.v2, fminf(v, x[e]));
+          v = fmaxf(v, x[e]);
+        }
       }
+      cb = m > b.v ? c : cb;
+      b.v = fmaxf(b.v, m);
+    }
+    if (cb >= 0) {                                     // the best's id inside its chunk
+      float x[kVec];
+      chunk_values<T>(*reinterpret_cast<const uint4*>(lr + (size_t)cb * kVec), x);
+      int e0 = kVec - 1;
+#pragma unroll
+      for (int e = kVec - 1; e >= 0; --e) e0 = x[e] == b.v ? e : e0;
+      b.i = cb * kVec + e0;
     }
   } else {
     for (int j = tid; j < vocab; j += kArgmaxThreads) consider(b, Elem<T>::load(lr, j), j);
+    if (tid < vocab && b.i == 0x7fffffff) b.i = tid;   // every value it saw was -inf
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -101,7 +140,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T* __restric
     Best r = sh[0];
     for (int w = 1; w < kArgmaxThreads / kWave; ++w) r = merge(r, sh[w]);
     pred[row] = r.i;
-    if (margins) margins[row] = vocab > 1 ? r.v - r.v2 : INFINITY;
+    if (MARGIN) margins[row] = vocab > 1 ? r.v - r.v2 : INFINITY;
   }
 }
 
@@ -148,12 +187,20 @@ hipError_t launch_accept(const int32_t* draft, int gamma, int batch, const int32
   // one argmax workgroup per logit row of every sequence ([batch][gamma+1]
   // rows back to back), then one commit wave per sequence
   const int rows = batch * (gamma + 1);
-  if (bf16)
-    argmax_rows<uint16_t><<<rows, kArgmaxThreads, 0, st>>>(
-        static_cast<const uint16_t*>(logits), vocab, gamma, gamma_dev, out_tokens, margins);
+  const auto* lb = static_cast<const uint16_t*>(logits);
+  const auto* lf = static_cast<const float*>(logits);
+  if (bf16 && margins)
+    argmax_rows<uint16_t, true><<<rows, kArgmaxThreads, 0, st>>>(lb, vocab, gamma, gamma_dev,
+                                                                 out_tokens, margins);
+  else if (bf16)
+    argmax_rows<uint16_t, false><<<rows, kArgmaxThreads, 0, st>>>(lb, vocab, gamma, gamma_dev,
+                                                                  out_tokens, margins);
+  else if (margins)
+    argmax_rows<float, true><<<rows, kArgmaxThreads, 0, st>>>(lf, vocab, gamma, gamma_dev,
+                                                              out_tokens, margins);
   else
-    argmax_rows<float><<<rows, kArgmaxThreads, 0, st>>>(static_cast<const float*>(logits), vocab,
-                                                       gamma, gamma_dev, out_tokens, margins);
+    argmax_rows<float, false><<<rows, kArgmaxThreads, 0, st>>>(lf, vocab, gamma, gamma_dev,
+                                                               out_tokens, margins);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   accept_commit<<<batch, 64, 0, st>>>(draft, gamma, gamma_dev, out_tokens, n_out, seq_len);

@@ -321,6 +321,41 @@ def test_accept_matches_oracle(lib, gamma, vocab, dtype, agree, ties):
         assert int(n_out.item()) == ref_n
         assert int(seq.item()) == 1000 + ref_n
         assert np.allclose(margins.cpu().numpy(), ref_m, rtol=1e-6, atol=1e-6)
+        # without margins the call takes its value-only path: same tokens
+        out2, n2 = lib.std_accept(draft.cuda(), logits.cuda())
+        torch.cuda.synchronize()
+        assert out2.cpu().numpy().tolist() == ref_out.tolist() and int(n2.item()) == ref_n
+
+
+@pytest.mark.parametrize("vocab", [152064, 1000, 1001, 9])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_accept_argmax_corners(lib, vocab, dtype):
+    """Argmax corners against the oracle, with and without margins: a row of
+    -inf (the lowest id wins, margin NaN), a maximum repeated across a
+    16-byte chunk boundary (ids 7 and 8) and at the ends of the row, the
+    maximum on the last id, and a row whose runner-up sits on the last id.
+    vocab 1001 and 9 take the element-by-element path."""
+    gamma = 5
+    gen = torch.Generator(device="cpu").manual_seed(vocab)
+    logits = torch.randn(gamma + 1, vocab, generator=gen)
+    logits[0] = -float("inf")
+    logits[1, 7] = logits[1, 8] = 9.0
+    logits[2, vocab - 1] = 9.0
+    logits[3, 0] = 9.0
+    logits[3, vocab - 1] = 8.5
+    logits[4, 0] = logits[4, vocab - 1] = 9.0
+    logits = logits.to(dtype)
+    draft = torch.tensor([0, 7, vocab - 1, 0, 0], dtype=torch.int32)
+    say(f"accept corners vocab={vocab} {dtype}")
+    ref_out, ref_n, ref_m, ref_pred = oracle.accept(draft.numpy(), f64(logits))
+    assert ref_pred[:5].tolist() == [0, 7, vocab - 1, 0, 0]       # premise of the case
+    margins = torch.empty(gamma + 1, dtype=torch.float32, device="cuda")
+    out, n_out = lib.std_accept(draft.cuda(), logits.cuda(), margins=margins)
+    out2, n2 = lib.std_accept(draft.cuda(), logits.cuda())
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tolist() == ref_out.tolist() and int(n_out.item()) == ref_n
+    assert out2.cpu().numpy().tolist() == ref_out.tolist() and int(n2.item()) == ref_n
+    assert np.allclose(margins.cpu().numpy(), ref_m, rtol=1e-6, atol=1e-6, equal_nan=True)
 
 
 def test_sparse_decode_reuses_one_workspace(lib):
