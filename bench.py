@@ -482,6 +482,15 @@ def main():
                 "unit": "TFLOP/s", "frac": round(sel_tflops * 1e12 / PEAK_BF16, 4),
                 "traffic": None, "kernel": "selection (std_select_topk)",
                 "ms_per_layer": round(sel_ms_layer, 3)}
+    # acceptance: (gamma + 1) bf16 logit rows of the vocabulary read per call,
+    # one call per cycle (argmax per row + commit); latency-bound at this size
+    acc_us = ph["accept_ms"] * 1e3 / max(cycles, 1)
+    acc_bytes = (G + 1) * vocab * 2
+    acc_roof = {"bound": "hbm", "achieved": round(acc_bytes / (acc_us * 1e-6) / 1e9, 1),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": round(acc_bytes / (acc_us * 1e-6) / PEAK_HBM, 4), "traffic": None,
+                "kernel": "acceptance (std_accept)", "bytes_per_launch": acc_bytes,
+                "us_per_launch": round(acc_us, 2)}
     phases = {"select": ph["select_ms"], "draft": ph["draft_ms"], "verify": ph["verify_ms"]}
     # The roofline object is the dense verify kernel: the single kernel with
     # the largest share of GPU time in the request (the kernel trace under
@@ -518,6 +527,7 @@ def main():
         "dense_attn": dense_roof,
         "sparse_attn": sparse_roof,
         "selection": sel_roof,
+        "accept": acc_roof,
         "phases_ms_per_step": {k: round(v / args.steps, 3) for k, v in
                                {**phases, "accept": ph["accept_ms"]}.items()},
         "accepted_tokens_per_cycle": round(ph["emitted"] / max(cycles, 1), 3),
