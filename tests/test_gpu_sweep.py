@@ -151,3 +151,95 @@ def test_sweep_case(lib, seed):
         ref_lse = oracle.row_lse(qt, kf, ctx).T
         assert max_abs(f64(out), ref) <= TOL["bf16"]
         assert max_abs(f64(lse), ref_lse) <= TOL_LSE
+
+
+# ------------------------------------------------------------ batched sweep
+N_BATCH_CASES = 16
+
+
+def draw_batch(seed):
+    """One batched case: B sequences of one layer shape, each with its own
+    valid length and draft length (host only)."""
+    r = np.random.default_rng(5000 + seed)
+    B = int(r.integers(2, 10))
+    hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4, 7, 8, 16]))
+    d = int(r.choice([64, 128]))
+    prefix = int(r.choice([0, int(r.integers(1, 80))]))
+    vis_len = int(r.integers(1, 4000))
+    kind = r.random()
+    if kind < 0.15:
+        topk = 0                                 # text keys only
+    elif kind < 0.3:
+        topk = vis_len
+    else:
+        topk = int(r.integers(1, vis_len + 1))
+        topk = min(topk, int(r.integers(1, 700))) if r.random() < 0.5 else topk
+    gamma = int(r.integers(1, 8))
+    # every length past the visual span and at least the verify's gamma + 1
+    base = prefix + vis_len + int(r.integers(8, 60))
+    lens = [base + int(r.integers(0, 300)) for _ in range(B)]
+    gammas = [int(r.integers(0, gamma + 1)) for _ in range(B)]
+    vocab = int(r.choice([512, 1000, 3001]))
+    return dict(B=B, hkv=hkv, hq=hkv * G, d=d, prefix=prefix, vis_len=vis_len, topk=topk,
+                gamma=gamma, lens=lens, gammas=gammas, vocab=vocab)
+
+
+def test_batch_sweep_draws_cover_the_corners():
+    cases = [draw_batch(s) for s in range(N_BATCH_CASES)]
+    assert {c["d"] for c in cases} == {64, 128}
+    assert any(c["topk"] == 0 for c in cases) and any(c["topk"] == c["vis_len"] for c in cases)
+    assert any(0 in c["gammas"] for c in cases)
+    assert any(c["hq"] // c["hkv"] == 16 for c in cases) and any(c["hq"] == c["hkv"] for c in cases)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(N_BATCH_CASES))
+def test_batch_sweep_case(lib, seed):
+    """The batched draft, verify and acceptance calls on one seeded draw,
+    every sequence at its own device length (and draft length for the
+    acceptance), against the oracle sequence by sequence."""
+    c = draw_batch(seed)
+    say(f"batch sweep seed={seed} {c}")
+    B, hq, hkv, d = c["B"], c["hq"], c["hkv"], c["d"]
+    prefix, vis_len, topk, gamma = c["prefix"], c["vis_len"], c["topk"], c["gamma"]
+    lens = c["lens"]
+    cap = max(lens) + 5
+    gen = torch.Generator(device="cpu").manual_seed(7000 + seed)
+    k = torch.randn(B, hkv, cap, d, generator=gen).bfloat16()
+    v = torch.randn(B, hkv, cap, d, generator=gen).bfloat16()
+    q = (torch.randn(B, hq, d, generator=gen) * 1.5).bfloat16()
+    n_q = gamma + 1
+    qv = (torch.randn(B, n_q, hq, d, generator=gen) * 1.5).bfloat16()
+    idx = torch.stack([torch.stack([torch.sort(torch.randperm(vis_len, generator=gen)[:topk])[0]
+                                    for _ in range(hkv)]) for _ in range(B)]).to(torch.int32)
+    idx = (idx + prefix).reshape(B, hkv, topk)
+    kd, vd = k.cuda(), v.cuda()
+    len_dev = torch.tensor(lens, dtype=torch.int32, device="cuda") - 1
+    out = lib.std_sparse_decode_attn_batch(q.cuda(), kd, vd, max(lens), prefix, vis_len,
+                                           idx.cuda(), len_dev=len_dev, len_offset=1)
+    outv = lib.std_dense_verify_attn_batch(qv.cuda(), kd, vd, max(lens), len_dev=len_dev,
+                                           len_offset=1)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kf, vf = f64(k[b]), f64(v[b])
+        ref = oracle.sparse_decode(f64(q[b]), kf, vf, lens[b], prefix, vis_len, idx[b].numpy())
+        assert max_abs(f64(out[b]), ref) <= TOL["bf16"], ("draft", b)
+        ref = oracle.dense_verify(f64(qv[b]), kf, vf, lens[b])
+        assert max_abs(f64(outv[b]), ref) <= TOL["bf16"], ("verify", b)
+    # acceptance with each sequence's own draft length
+    import synth
+    cases = [synth.accept_case(gamma, c["vocab"], 0.8, seed=9000 + 10 * seed + b,
+                               dtype=torch.bfloat16, n_ties=b % 2) for b in range(B)]
+    draft = torch.stack([x[0] for x in cases]).cuda()
+    logits = torch.stack([x[1] for x in cases]).contiguous().cuda()
+    gdev = torch.tensor(c["gammas"], dtype=torch.int32, device="cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    toks, n_out = lib.std_accept_batch(draft, logits, seq_len=seq, gamma_dev=gdev)
+    torch.cuda.synchronize()
+    for b in range(B):
+        g = c["gammas"][b]
+        ref_toks, ref_n, _, _ = oracle.accept(cases[b][0][:g].numpy(), f64(cases[b][1][:g + 1]))
+        got = toks[b].cpu().numpy().tolist()
+        assert got[:g + 1] == ref_toks.tolist() and got[g + 1:] == [-1] * (gamma - g), b
+        assert int(n_out[b]) == ref_n and int(seq[b]) == lens[b] + ref_n, b
