@@ -96,9 +96,24 @@ std_status_t check_sparse(const std_attn_shape_t* s, const std_kv_t* kv, std_vis
   return ok();
 }
 
-int sparse_splits(const std_kv_t* kv, std_vis_t vis, int topk) {
+// Entry passes per draft workgroup: one kSparseChunk-entry chunk, or two
+// when a batch's grid would otherwise need more than one round of the
+// machine's resident workgroups (two per CU).  Two passes load both
+// chunks' rows before using either, so a workgroup still waits about one
+// memory latency while the grid halves (bf16 MFMA path only; the vector
+// ALU path takes one chunk per split).
+int sparse_passes(const std_attn_shape_t* s, const std_kv_t* kv, std_vis_t vis, int topk,
+                  int batch) {
+  if (batch <= 1 || kv->dtype != STD_DTYPE_BF16 || s->n_q_heads / s->n_kv_heads > 16) return 1;
+  const long long L = sparse_list_len(kv->len, vis.vis_start, vis.vis_len, topk);
+  const long long wg = (long long)batch * s->n_kv_heads * ((L + kSparseChunk - 1) / kSparseChunk);
+  return wg > 2 * 256 ? 2 : 1;
+}
+
+int sparse_splits(const std_kv_t* kv, std_vis_t vis, int topk, int passes = 1) {
   const int L = sparse_list_len(kv->len, vis.vis_start, vis.vis_len, topk);
-  return (L + kSparseChunk - 1) / kSparseChunk;
+  const int per = kSparseChunk * passes;
+  return (L + per - 1) / per;
 }
 
 // One sequence: dense_split_count.  A batch of several sequences runs in
@@ -300,7 +315,8 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t bat
                            const int32_t* gamma_dev, int32_t step, void* out, void* ws,
                            size_t ws_bytes, void* stream) {
   TRY(check_sparse_args(s, q, batch, kv, vis, idx, topk, gamma_dev, step, out));
-  const int splits = sparse_splits(kv, vis, topk);
+  const int passes = sparse_passes(s, kv, vis, topk, batch);
+  const int splits = sparse_splits(kv, vis, topk, passes);
   const SplitWorkspace w = split_workspace(splits, batch * s->n_q_heads, s->head_dim);
   TRY(check_ws(ws, ws_bytes, w.bytes()));
   AttnArgs a{};
@@ -317,7 +333,7 @@ std_status_t sparse_decode(const std_attn_shape_t* s, const void* q, int32_t bat
   a.vis_start = vis.vis_start; a.vis_len = vis.vis_len; a.topk = topk;
   a.ml = static_cast<float*>(ws);
   a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(w.ml_bytes));
-  a.splits = splits; a.chunk = kSparseChunk;
+  a.splits = splits; a.chunk = kSparseChunk; a.passes = passes;
   return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -411,7 +427,8 @@ std_status_t std_sparse_decode_attn_noalloc(const std_attn_shape_t* s, const voi
 size_t std_sparse_decode_batch_workspace(const std_attn_shape_t* s, int32_t batch,
                                          const std_kv_t* kv, std_vis_t vis, int32_t topk) {
   if (check_sparse_call(s, kv, vis, topk, batch) != STD_OK) return 0;
-  return split_workspace(sparse_splits(kv, vis, topk), batch * s->n_q_heads, s->head_dim)
+  return split_workspace(sparse_splits(kv, vis, topk, sparse_passes(s, kv, vis, topk, batch)),
+                         batch * s->n_q_heads, s->head_dim)
       .bytes();
 }
 

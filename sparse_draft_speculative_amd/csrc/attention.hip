@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
 // workgroup runs once.
 constexpr int kSparseWaves = kSparseChunk / kSparseEntriesPerWave;
 
-template <int D>
+template <int D, int P>
 __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   constexpr int STAGE = kSparseWaves * 2 * REGION * 2;
   constexpr int XCH = kSparseWaves * 64 * XS * 4;
   __shared__ __align__(16) uint8_t smem_raw[STAGE > XCH ? STAGE : XCH];
-  __shared__ int pos_s[kSparseChunk];
+  __shared__ int pos_s[kSparseChunk * P];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;   // split, KV head, sequence
@@ -472,23 +472,26 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   const int h = g * G + (row_ok ? col : 0);
   uint16_t* Ks = smem + wave * 2 * REGION;
   uint16_t* Vs = Ks + REGION;
-  int* pw = pos_s + wave * EW;
+  int* pw = pos_s + wave * EW * P;
 
   // Positions come from the list at the host bound (entries past it re-read
   // its last row), so the index reads and the row gathers do not wait for
   // the device length; entries past the actual list are masked below.
   KeyList kl{true, idx + (size_t)g * topk, vis_start, vis_end, topk};
   const int n_bound = vis_start + topk + max(0, lsrc.max - vis_end);
-  const int e0 = s * kSparseChunk + wave * EW;   // first entry of this wave
-  // lane EW fetches the device length beside the index reads.  An opaque
+  // A workgroup takes P consecutive chunks of kSparseChunk entries; in pass
+  // p wave w reduces entries e0 + p * kSparseChunk + [0, EW).
+  const int e0 = s * (kSparseChunk * P) + wave * EW;   // this wave's first entry
+  // lane 63 fetches the device length beside the index reads.  An opaque
   // zero lane offset makes it a vector load: a scalar load would be waited
   // for together with the argument loads (scalar loads complete out of
   // order), i.e. before anything else is issued.
   int zero_v;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
   int len_raw = 0;
-  if (lane == EW) len_raw = lsrc.ptr()[zero_v];
-  if (lane < EW) pw[lane] = kl.pos(min(e0 + lane, n_bound - 1));
+  if (lane == 63) len_raw = lsrc.ptr()[zero_v];
+  if (lane < EW * P)
+    pw[lane] = kl.pos(min(e0 + (lane / EW) * kSparseChunk + lane % EW, n_bound - 1));
   // The query operand: padding columns (G < 16) read a valid row (head g*G)
   // unconditionally, so the loads need no merge and stay in flight beside
   // the index reads; their results are never stored.
@@ -503,48 +506,61 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   const uint16_t* kh = k + (size_t)g * capacity * D;
   const uint16_t* vh = v + (size_t)g * capacity * D;
   // gathered rows load in their natural chunk order (short address path
-  // after the index read); the swizzle is applied to the LDS stores
-  u32x4_t kreg[NL], vreg[NL];
+  // after the index read); the swizzle is applied to the LDS stores.  The
+  // rows of every pass are loaded before any is used, so P passes wait
+  // about one memory latency.
+  u32x4_t kreg[P][NL], vreg[P][NL];
 #pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const int cl = lane + 64 * u;
-    const int row = cl / CPR, chunk = cl % CPR;
-    const size_t base = (size_t)pw[row] * D + (chunk << 3);
-    kreg[u] = *reinterpret_cast<const u32x4_t*>(kh + base);
-    vreg[u] = *reinterpret_cast<const u32x4_t*>(vh + base);
-  }
+  for (int ps = 0; ps < P; ++ps)
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int cl = lane + 64 * u;
+      const int row = cl / CPR, chunk = cl % CPR;
+      const size_t base = (size_t)pw[ps * EW + row] * D + (chunk << 3);
+      kreg[ps][u] = *reinterpret_cast<const u32x4_t*>(kh + base);
+      vreg[ps][u] = *reinterpret_cast<const u32x4_t*>(vh + base);
+    }
   // Entries past the actual list read rows the cache need not hold finite
   // values in: their scores are masked by selects below, and their V rows
   // are stored as zeros so that 0 * V stays 0 in the PV product.
-  const int len = lsrc.resolve(__builtin_amdgcn_readlane(len_raw, EW));
+  const int len = lsrc.resolve(__builtin_amdgcn_readlane(len_raw, 63));
   const int n_entries = vis_start + topk + max(0, len - vis_end);
-#pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const int cl = lane + 64 * u;
-    const int row = cl / CPR, chunk = cl % CPR;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4_t*>(Ks + Tile<D>::off_k(row, chunk)) = kreg[u];
-    *reinterpret_cast<u32x4_t*>(Vs + Tile<D>::off_v(row, chunk)) =
-        e0 + row < n_entries ? vreg[u] : zero;
-  }
-  // the wave reads back only its own region: no workgroup barrier needed
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS stores done
-  __builtin_amdgcn_wave_barrier();
 
   float m = -INFINITY, lsum = 0.f;
   floatx4_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  if (e0 < n_entries) {
-    floatx4_t sacc[NKB];
-    TM::scores(Ks, qb, col, grp, sacc);
-    float x[4 * NKB], p[4 * NKB];
 #pragma unroll
-    for (int j = 0; j < 4 * NKB; ++j)
-      x[j] = e0 + (j >> 2) * 16 + 4 * grp + (j & 3) < n_entries ? sacc[j >> 2][j & 3] * c
-                                                                 : -INFINITY;
-    online_update<DB, 4 * NKB>(x, p, m, lsum, oacc);
-    TM::pv(Vs, p, col, grp, oacc);
+  for (int ps = 0; ps < P; ++ps) {
+    const int ep = e0 + ps * kSparseChunk;     // this pass's first entry (wave-uniform)
+    // the previous pass's LDS reads have returned before its rows are overwritten
+    if (ps > 0) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int cl = lane + 64 * u;
+      const int row = cl / CPR, chunk = cl % CPR;
+      const u32x4_t zero = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(Ks + Tile<D>::off_k(row, chunk)) = kreg[ps][u];
+      *reinterpret_cast<u32x4_t*>(Vs + Tile<D>::off_v(row, chunk)) =
+          ep + row < n_entries ? vreg[ps][u] : zero;
+    }
+    // the wave reads back only its own region: no workgroup barrier needed
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS stores done
+    __builtin_amdgcn_wave_barrier();
+    if (ep < n_entries) {
+      floatx4_t sacc[NKB];
+      TM::scores(Ks, qb, col, grp, sacc);
+      float x[4 * NKB], p[4 * NKB];
+#pragma unroll
+      for (int j = 0; j < 4 * NKB; ++j)
+        x[j] = ep + (j >> 2) * 16 + 4 * grp + (j & 3) < n_entries ? sacc[j >> 2][j & 3] * c
+                                                                  : -INFINITY;
+      online_update<DB, 4 * NKB>(x, p, m, lsum, oacc);
+      TM::pv(Vs, p, col, grp, oacc);
+    }
   }
   lsum = sum_over_groups(lsum);
 
@@ -783,10 +799,17 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const LenSrc lsrc{a.len, a.len_dev, a.len_off, a.len_lo};
   if (a.sparse) {
     const int batch = a.batch > 1 ? a.batch : 1;
-    sparse_mfma_kernel<D><<<dim3(a.splits, a.hkv, batch), 64 * kSparseWaves, 0, st>>>(
-        q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
-        a.topk, lsrc, a.gamma_dev, a.step, a.splits, batch * a.hq,
-        reinterpret_cast<float2*>(a.ml), a.o);
+    const dim3 grid(a.splits, a.hkv, batch);
+    if (a.passes == 2)
+      sparse_mfma_kernel<D, 2><<<grid, 64 * kSparseWaves, 0, st>>>(
+          q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
+          a.topk, lsrc, a.gamma_dev, a.step, a.splits, batch * a.hq,
+          reinterpret_cast<float2*>(a.ml), a.o);
+    else
+      sparse_mfma_kernel<D, 1><<<grid, 64 * kSparseWaves, 0, st>>>(
+          q, k, v, a.hq, a.hkv, a.capacity, c, a.idx, a.vis_start, a.vis_start + a.vis_len,
+          a.topk, lsrc, a.gamma_dev, a.step, a.splits, batch * a.hq,
+          reinterpret_cast<float2*>(a.ml), a.o);
   } else {
     const int batch = a.batch > 1 ? a.batch : 1;
     const int rows_group = a.n_q * (a.hq / a.hkv);

@@ -99,6 +99,7 @@ struct AttnArgs {
   float* o;             // [splits][rows][D]
   int splits;
   int chunk;            // keys (dense) or list entries (sparse) per split
+  int passes;           // sparse MFMA path: kSparseChunk-entry passes per split (1 or 2)
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
