@@ -127,7 +127,11 @@ int dense_splits(const std_attn_shape_t* s, const std_kv_t* kv, int n_q, int* ch
   *chunk = 64;                                   // tile size; splits interleave tiles
   if (batch <= 1) return dense_split_count(kv->len, s->n_kv_heads);
   const long long tiles = (kv->len + 63) / 64;
-  const long long row_blocks = ((long long)n_q * (s->n_q_heads / s->n_kv_heads) + 63) / 64;
+  // workgroups take 64 query rows, or 128 when a group has more than 64 at
+  // head_dim 128
+  const long long rows = (long long)n_q * (s->n_q_heads / s->n_kv_heads);
+  const long long per_block = rows > 64 && s->head_dim == 128 ? 128 : 64;
+  const long long row_blocks = (rows + per_block - 1) / per_block;
   const long long wg = (long long)batch * s->n_kv_heads * row_blocks;   // per split
   const long long rounds = tiles * wg >= 128LL * 512 ? 2 : 1;
   long long S = 256 * rounds / wg;

@@ -195,18 +195,18 @@ constexpr int kDenseBufs = 3;
 // into the swizzled LDS layout of Tile<D>.  Thread tid fills 16-byte slots
 // 512u + tid of each tensor; a slot's row and physical chunk give the
 // logical chunk by the (self-inverse) XOR swizzle.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void dense_issue_tile(uint16_t* ks, uint16_t* vs, const uint16_t* kh,
                                                  const uint16_t* vh, int t0, int len, int tid,
                                                  int wave) {
   constexpr int CPR = D / 8;
-  constexpr int LPT = 64 * CPR / kDenseThreads;
+  constexpr int LPT = 64 * CPR / NT;
 #pragma unroll
   for (int u = 0; u < LPT; ++u) {
-    const int slot = kDenseThreads * u + tid;
+    const int slot = NT * u + tid;
     const int row = slot / CPR, phys = slot % CPR;
     const size_t base = (size_t)min(t0 + row, len - 1) * D;
-    const uint32_t dst = (kDenseThreads * u + 64 * wave) * 16;
+    const uint32_t dst = (NT * u + 64 * wave) * 16;
     dma16_stream(kh + base + (Tile<D>::slot_k(row, phys) << 3), lds_addr(ks) + dst);
     dma16_stream(vh + base + (Tile<D>::slot_v(row, phys) << 3), lds_addr(vs) + dst);
   }
@@ -284,22 +284,31 @@ __device__ __forceinline__ void dense_step(const uint16_t* Ks, const uint16_t* V
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
+// W = 1: 512 threads, 64 query rows per workgroup; W = 2 (head_dim 128 with
+// more than 64 rows in a group, e.g. gamma + 1 >= 10 queries of a 7-head
+// group): 1,024 threads and 128 rows, so each K/V tile is still read once
+// for all of them (at head_dim 64 such groups keep 64-row blocks).
+template <int D, int W>
+__global__ __launch_bounds__(kDenseThreads * W, 1) void dense_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, LenSrc lsrc, int n_q, float c,
     int splits, float2* __restrict__ ml, float* __restrict__ o, int rows_total) {
   constexpr int DB = D / 16;
   constexpr int CPR = D / 8;
   constexpr int TILE = 64 * D;                       // elements of one K or V tile
-  constexpr int LPT = 64 * CPR / kDenseThreads;      // copies per thread per tensor per tile
-  __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE + 64 * D];   // [buffer][K, V], Q
+  constexpr int NT = kDenseThreads * W;              // threads per workgroup
+  constexpr int ROWS = 64 * W;                       // query rows per workgroup
+  constexpr int LPT = 64 * CPR / NT;                 // copies per thread per tensor per tile
+  constexpr int LQ = ROWS * CPR / NT;                // query-row copies per thread
+  static_assert(LPT >= 1 && LPT * NT == 64 * CPR && LQ * NT == ROWS * CPR,
+                "every thread issues the same whole number of copies");
+  __shared__ __align__(16) uint16_t smem[kDenseBufs * 2 * TILE + ROWS * D];   // [buffer][K, V], Q
 
   const int G = hq / hkv;
   const int Rg = n_q * G;
-  // grid z = (sequence, 64-row block); sequence b of a batch has its own
+  // grid z = (sequence, ROWS-row block); sequence b of a batch has its own
   // queries, cache and length (one sequence: b = 0)
-  const int n_rb = (Rg + 63) / 64;
+  const int n_rb = (Rg + ROWS - 1) / ROWS;
   const int s = blockIdx.x, g = blockIdx.y, rb = blockIdx.z % n_rb, b = blockIdx.z / n_rb;
   q += (size_t)b * n_q * hq * D;
   k += (size_t)b * hkv * capacity * D;
@@ -309,24 +318,24 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kh = wave & 1, nbw = wave >> 1;
   const int col = lane & 15, grp = lane >> 4;
-  const int r0 = rb * 64 + nbw * 16;                 // first query row of this wave
+  const int r0 = rb * ROWS + nbw * 16;               // first query row of this wave
   const bool active = r0 < Rg;                       // wave-uniform
   const int rho = r0 + col;
   const bool rok = rho < Rg;
   const int qi = rok ? rho / G : 0;
   const int hh = g * G + (rok ? rho % G : 0);
-  // The row block's 64 query rows go to LDS by direct-to-LDS copies ahead
-  // of the first K/V tiles, so their latency overlaps the tiles' (rows past
+  // The row block's query rows go to LDS by direct-to-LDS copies ahead of
+  // the first K/V tiles, so their latency overlaps the tiles' (rows past
   // Rg re-read row Rg - 1; their results are never stored).
   uint16_t* qs = smem + kDenseBufs * 2 * TILE;
 #pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int slot = kDenseThreads * u + tid;
+  for (int u = 0; u < LQ; ++u) {
+    const int slot = NT * u + tid;
     const int row = slot / CPR, phys = slot % CPR;
-    const int rr = min(rb * 64 + row, Rg - 1);
+    const int rr = min(rb * ROWS + row, Rg - 1);
     const uint16_t* src = q + ((size_t)(rr / G) * hq + g * G + rr % G) * D +
                           (Tile<D>::slot_k(row, phys) << 3);
-    dma16(src, lds_addr(qs) + (kDenseThreads * u + 64 * wave) * 16);
+    dma16(src, lds_addr(qs) + (NT * u + 64 * wave) * 16);
   }
 
   // (the device length, loaded at entry, is first needed here)
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
   constexpr int kInFlight = 2 * (kDenseBufs - 2) * LPT;   // copies of B-2 tiles
 #pragma unroll
   for (int b = 0; b < kDenseBufs - 1; ++b)
-    dense_issue_tile<D>(kbuf(b), vbuf(b), khd, vhd, tile_key(b), len, tid, wave);
+    dense_issue_tile<D, NT>(kbuf(b), vbuf(b), khd, vhd, tile_key(b), len, tid, wave);
   // the query rows have landed (the prologue's tile copies may still be in
   // flight); each wave takes its 16 rows' operand
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kDenseBufs - 1) * LPT));
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInFlight));
         __syncthreads();
         const int nb = (b + kDenseBufs - 1) % kDenseBufs;
-        dense_issue_tile<D>(kbuf(nb), vbuf(nb), khd, vhd, tile_key(i + b + kDenseBufs - 1), len,
+        dense_issue_tile<D, NT>(kbuf(nb), vbuf(nb), khd, vhd, tile_key(i + b + kDenseBufs - 1), len,
                             tid, wave);
         if (active)
           dense_step<D>(kbuf(b), vbuf(b), qb, kh, tile_key(i + b), len, safe_end, qpos, c, col,
@@ -388,6 +397,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_mfma_kernel(
 
   // merge the two key halves: odd waves hand (m, l, O) to their even partner
   constexpr int XS = 2 + 4 * DB;                     // floats per lane
+  static_assert(4 * W * 64 * XS * 4 <= kDenseBufs * 2 * TILE * 2, "the merge fits the tile buffers");
   float* xch = reinterpret_cast<float*>(smem);
   if (kh == 1 && active) {
     float* dst = xch + (size_t)(nbw * 64 + lane) * XS;
@@ -813,11 +823,19 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   } else {
     const int batch = a.batch > 1 ? a.batch : 1;
     const int rows_group = a.n_q * (a.hq / a.hkv);
+    if constexpr (D == 128) {
+      if (rows_group > 64) {
+        dim3 grid(a.splits, a.hkv, batch * ((rows_group + 127) / 128));
+        dense_mfma_kernel<D, 2><<<grid, kDenseThreads * 2, 0, st>>>(
+            q, k, v, a.hq, a.hkv, a.capacity, lsrc, a.n_q, c, a.splits,
+            reinterpret_cast<float2*>(a.ml), a.o, batch * a.n_q * a.hq);
+        return hipGetLastError();
+      }
+    }
     dim3 grid(a.splits, a.hkv, batch * ((rows_group + 63) / 64));
-    dense_mfma_kernel<D><<<grid, kDenseThreads, 0, st>>>(q, k, v, a.hq, a.hkv, a.capacity, lsrc,
-                                                         a.n_q, c, a.splits,
-                                                         reinterpret_cast<float2*>(a.ml), a.o,
-                                                         batch * a.n_q * a.hq);
+    dense_mfma_kernel<D, 1><<<grid, kDenseThreads, 0, st>>>(
+        q, k, v, a.hq, a.hkv, a.capacity, lsrc, a.n_q, c, a.splits,
+        reinterpret_cast<float2*>(a.ml), a.o, batch * a.n_q * a.hq);
   }
   return hipGetLastError();
 }
