@@ -75,6 +75,8 @@ def parse():
                     help="skip the selection timing with a caller-supplied row LSE")
     ap.add_argument("--no-toy", action="store_true",
                     help="skip the end-to-end toy decoder measurement")
+    ap.add_argument("--no-gamma-sweep", action="store_true",
+                    help="skip the draft-length sweep (verify timed at gamma + 1 queries)")
     ap.add_argument("--sync-each-cycle", action="store_true",
                     help="read each cycle's n_out before launching the next (the blocking "
                          "loop, for comparison)")
@@ -465,6 +467,11 @@ def main():
     sel_tflops = select_flops(cfg) / (sel_ms_layer * 1e-3) / 1e12
 
     probe = read_probe(sd, attn_bytes_dense(cfg, cfg.verify_len, G + 1))
+    acc_us = ph["accept_ms"] * 1e3 / max(cycles, 1)
+    gsweep = None
+    if not args.no_gamma_sweep:
+        say("# draft-length sweep")
+        gsweep = gamma_sweep(sd, cfg, layers, st, sp_call_us, acc_us, dense_ms_per_tok)
 
     def hbm_roof(gbps, bytes_per_launch):
         return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9,
@@ -484,7 +491,6 @@ def main():
                 "ms_per_layer": round(sel_ms_layer, 3)}
     # acceptance: (gamma + 1) bf16 logit rows of the vocabulary read per call,
     # one call per cycle (argmax per row + commit); latency-bound at this size
-    acc_us = ph["accept_ms"] * 1e3 / max(cycles, 1)
     acc_bytes = (G + 1) * vocab * 2
     acc_roof = {"bound": "hbm", "achieved": round(acc_bytes / (acc_us * 1e-6) / 1e9, 1),
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s",
@@ -550,6 +556,7 @@ def main():
         "batched_decode": batch_cycles,
         "batched_decode_per_sequence_gamma": batch_mixed,
         "hbm_read_probe": probe,
+        "gamma_sweep": gsweep,
         "projection": projection(cycle_ms, G, dense_ms_per_tok,
                                  L * attn_bytes_sparse(cfg, cfg.ctx + 1),
                                  L * attn_bytes_dense(cfg, cfg.verify_len, G + 1),
@@ -800,6 +807,82 @@ def projection(cycle_ms, gamma, dense_ms_per_tok, step_bytes, verify_bytes, dens
                              "mb_per_token": round(cycle_bytes / e / 1e6, 1),
                              "io_reduction_vs_dense": round(dense_tok_bytes * e / cycle_bytes, 3)}
     return out
+
+
+def gamma_sweep(sd, cfg, layers, st, sp_call_us, acc_us, dense_ms_per_tok,
+                gammas=(2, 4, 6, 8, 9, 10, 12, 14, 16), reps=5):
+    """Draft length against the projected attention-only decode rate (the
+    pages' ablation finds the speed-up rising with gamma up to about 9,
+    technical summary, Experimental results).  For each gamma the verify
+    pass is timed: 28 dense calls with gamma + 1 queries at ctx + gamma + 1
+    keys (graph-replayed on the bench stream).  A cycle is then gamma draft
+    steps at the measured per-call draft time (its list grows by one entry
+    per step, which the call time does not see), that verify pass and one
+    acceptance at the measured call time (latency-bound: its (gamma + 1)
+    logit rows change it little).  Tokens per cycle under independent
+    acceptance, E = (1 - alpha^(gamma+1)) / (1 - alpha), over the cycle time
+    gives the rate for alpha in {0.8, 0.9, 0.95}; selection is not included."""
+    import torch
+    L = len(layers)
+    dev = layers[0]["k"].device
+    shape = sd.attn_shape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+    cap = cfg.capacity
+    nq_max = max(gammas) + 1
+    if cfg.ctx + nq_max > cap:
+        raise ValueError("cache capacity too small for the sweep")
+    ws = torch.zeros(max(sd.std_dense_verify_workspace(shape, nq_max, layers[0]["k"], cap), 256),
+                     dtype=torch.uint8, device=dev)
+    seq = torch.full((1,), cfg.ctx, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    draft_step_ms = sp_call_us * L / 1e3
+    rows, best = [], {}
+    for g in gammas:
+        nq = g + 1
+        qs = [torch.randn(nq, cfg.n_q_heads, cfg.head_dim, device=dev, generator=gen)
+              .to(torch.bfloat16) for _ in range(L)]
+        out = torch.empty(nq, cfg.n_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
+        calls = [sd.prepare_dense_verify_dlen(qs[l], lay["k"], lay["v"], out, ws, seq, nq,
+                                              max_len=cap, stream=st)
+                 for l, lay in enumerate(layers)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            for c in calls:                    # warm-up outside the capture
+                c()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(st):
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        verify_ms = e0.elapsed_time(e1) / reps
+        call_us = verify_ms * 1e3 / L
+        vbytes = attn_bytes_dense(cfg, cfg.ctx + nq, nq)
+        t = g * draft_step_ms + verify_ms + acc_us / 1e3
+        row = {"gamma": g, "verify_us_per_call": round(call_us, 2),
+               "verify_frac": round(vbytes / (call_us * 1e-6) / PEAK_HBM, 4),
+               "cycle_ms": round(t, 4)}
+        for a in (0.8, 0.9, 0.95):
+            e = (1 - a ** (g + 1)) / (1 - a)
+            row[f"alpha_{a}"] = {"tokens_per_s": round(e * 1e3 / t, 1),
+                                 "speedup_vs_dense": round(e * dense_ms_per_tok / t, 3)}
+            if a not in best or e / t > best[a][1]:
+                best[a] = (g, e / t)
+        rows.append(row)
+        del graph, calls, qs, out
+    del ws
+    torch.cuda.empty_cache()
+    return {"label": "attention-only, projected from measured calls",
+            "draft_step_ms": round(draft_step_ms, 4), "accept_ms": round(acc_us / 1e3, 4),
+            "rows": rows,
+            "best_gamma": {f"alpha_{a}": best[a][0] for a in (0.8, 0.9, 0.95)}}
 
 
 def toy_e2e(n_new=256, gammas=(2, 4, 6), seed=0):
