@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kDenseThreads * W, 1) void dense_mfma_kernel(
 constexpr int kSparseWaves = kSparseChunk / kSparseEntriesPerWave;
 
 template <int D, int P>
-__global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
+__global__ __launch_bounds__(64 * kSparseWaves, 2) void sparse_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int hq, int hkv, int capacity, float c,
     const int32_t* __restrict__ idx, int vis_start, int vis_end, int topk, LenSrc lsrc,
@@ -518,7 +518,9 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
   // gathered rows load in their natural chunk order (short address path
   // after the index read); the swizzle is applied to the LDS stores.  The
   // rows of every pass are loaded before any is used, so P passes wait
-  // about one memory latency.
+  // about one memory latency.  The loads are non-temporal: a call reads each
+  // row once, and at 28 layers a draft step's rows do not stay cached until
+  // the next step anyway.
   u32x4_t kreg[P][NL], vreg[P][NL];
 #pragma unroll
   for (int ps = 0; ps < P; ++ps)
@@ -527,8 +529,8 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_mfma_kernel(
       const int cl = lane + 64 * u;
       const int row = cl / CPR, chunk = cl % CPR;
       const size_t base = (size_t)pw[ps * EW + row] * D + (chunk << 3);
-      kreg[ps][u] = *reinterpret_cast<const u32x4_t*>(kh + base);
-      vreg[ps][u] = *reinterpret_cast<const u32x4_t*>(vh + base);
+      kreg[ps][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kh + base));
+      vreg[ps][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vh + base));
     }
   // Entries past the actual list read rows the cache need not hold finite
   // values in: their scores are masked by selects below, and their V rows

@@ -100,7 +100,11 @@ def test_dense_single_query_decode(lib, name):
 @pytest.mark.parametrize("hq,hkv,d,dtype,n_q,length,cap", [
     (8, 2, 64, "bf16", 7, 8390, 8400),      # toy-decoder shape, ragged length
     (28, 4, 128, "bf16", 1, 65, 70),        # tiny cache, single query
-    (28, 4, 128, "bf16", 100, 3000, 3001),  # many query rows: several 64-row blocks
+    (28, 4, 128, "bf16", 100, 3000, 3001),  # many query rows: several 128-row blocks
+    (28, 4, 128, "bf16", 10, 5000, 5003),   # gamma = 9: 70 rows, one 128-row block
+    (28, 4, 128, "bf16", 18, 1100, 1118),   # 126 rows, one 128-row block
+    (28, 4, 128, "bf16", 19, 1500, 1519),   # 133 rows: two 128-row blocks, the second ragged
+    (8, 1, 64, "bf16", 9, 700, 710),        # 72 rows at head_dim 64: two 64-row blocks
     (4, 4, 64, "f32", 3, 777, 800),         # G = 1, fp32
     (32, 1, 128, "bf16", 5, 4097, 4100),    # G = 32
     (6, 2, 128, "f32", 2, 130, 130),
@@ -132,6 +136,24 @@ def test_dense_verify_is_deterministic_and_row_invariant(lib):
                                     cfg.verify_len)
     torch.cuda.synchronize()
     assert torch.equal(one[0], a[-1])
+
+
+@pytest.mark.parametrize("n_q", [10, 17])
+def test_dense_verify_rows_past_64_are_row_invariant(lib, n_q):
+    """Groups of more than 64 query rows (head_dim 128) take 128-row
+    workgroups; each row's arithmetic is the same as in a 64-row block, so
+    the last verify row equals the single-query call bitwise."""
+    g = torch.Generator(device="cuda").manual_seed(n_q)
+    k = torch.randn(4, 9000, 128, generator=g, device="cuda").bfloat16()
+    v = torch.randn(4, 9000, 128, generator=g, device="cuda").bfloat16()
+    q = (torch.randn(n_q, 28, 128, generator=g, device="cuda") * 1.5).bfloat16()
+    length = 8990
+    a = lib.std_dense_verify_attn(q, k, v, length)
+    one = lib.std_dense_verify_attn(q[-1:].contiguous(), k, v, length)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], a[-1])
+    ref = oracle.dense_verify(f64(q), f64(k), f64(v), length)
+    assert max_abs(f64(a), ref) <= TOL["bf16"]
 
 
 # ---------------------------------------------------------------- sparse draft
