@@ -51,6 +51,11 @@ def make_batch(B, hq, hkv, d, prefix, vis_len, cap, topk, seed):
     (3, 28, 4, 128, 0, 2000, 256, (2100, 2037, 2299)),
     (5, 8, 2, 64, 17, 900, 100, (1000, 917, 950, 999, 1040)),
     (2, 16, 1, 128, 0, 3000, 0, (3001, 3100)),     # K = 0: text keys only
+    # grids above one round of resident workgroups (B x H_kv x 128-entry
+    # chunks > 512): two chunks per workgroup, the last split's second
+    # chunk partly or wholly past each sequence's list
+    (6, 28, 4, 128, 0, 20000, 2048, (22001, 21500, 22100, 21337, 22048, 21900)),
+    (12, 16, 2, 64, 40, 30000, 3000, tuple(30100 + 37 * b for b in range(12))),
 ])
 def test_batched_sparse_matches_oracle(lib, B, hq, hkv, d, prefix, vis_len, topk, lens):
     cap = max(lens) + 8
@@ -114,6 +119,26 @@ def test_batched_dense_verify_matches_oracle(lib, B, hq, hkv, d, n_q, lens):
     out = lib.std_dense_verify_attn_batch(q, k, v, max(lens), len_dev=len_dev, len_offset=4)
     torch.cuda.synchronize()
     for b in range(B):
+        ref = oracle.dense_verify(f64(q[b]), f64(k[b]), f64(v[b]), lens[b])
+        assert np.max(np.abs(f64(out[b]) - ref)) <= TOL, b
+
+
+def test_batched_dense_verify_two_rounds_matches_oracle(lib):
+    """A batch whose workgroups would each stream at least 128 tiles in one
+    round of 256 (16 sequences x 8 KV heads, 516 tiles of 64 keys) takes
+    two rounds of workgroups: every sequence still matches the oracle."""
+    B, hq, hkv, d, n_q = 16, 16, 8, 128, 4
+    lens = [32800 + 13 * b for b in range(B)]
+    cap = max(lens) + 3
+    g = torch.Generator(device="cuda").manual_seed(424)
+    k = torch.randn(B, hkv, cap, d, generator=g, device="cuda").bfloat16()
+    v = torch.randn(B, hkv, cap, d, generator=g, device="cuda").bfloat16()
+    q = (torch.randn(B, n_q, hq, d, generator=g, device="cuda") * 1.5).bfloat16()
+    len_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    say(f"batched dense two rounds B={B} hq={hq} hkv={hkv} n_q={n_q} max len {max(lens)}")
+    out = lib.std_dense_verify_attn_batch(q, k, v, max(lens), len_dev=len_dev, len_offset=0)
+    torch.cuda.synchronize()
+    for b in (0, 7, B - 1):
         ref = oracle.dense_verify(f64(q[b]), f64(k[b]), f64(v[b]), lens[b])
         assert np.max(np.abs(f64(out[b]) - ref)) <= TOL, b
 
