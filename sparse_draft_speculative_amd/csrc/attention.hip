@@ -430,8 +430,10 @@ __global__ __launch_bounds__(kDenseThreads * W, 1) void dense_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Sparse draft step: grid (split of kSparseChunk key-list entries, KV head),
-// kSparseWaves waves of kSparseEntriesPerWave entries each.
+// Sparse draft step: grid (split of P * kSparseChunk key-list entries, KV
+// head, sequence), kSparseWaves waves of kSparseEntriesPerWave entries per
+// pass; P = 1, or 2 for a batch whose grid would exceed one round of
+// resident workgroups (two per CU).
 //
 // Each wave gathers its entries of the head's key list (prefix + selected
 // visual positions + tail) into its own LDS region -- one contiguous
