@@ -75,6 +75,25 @@ def test_dlen_calls_match_oracle(lib, c2):
         assert max_abs(f64(outv), refv) <= TOL
 
 
+@pytest.mark.parametrize("n_q", [10, 17])
+def test_dlen_long_verify_matches_oracle(lib, c2, n_q):
+    """Draft lengths of 9 and 16 (70 and 119 query rows per KV head: the
+    128-row verify workgroups) with the length read on the device."""
+    cfg, lay, _, _ = c2
+    kf, vf = f64(lay["k"]), f64(lay["v"])
+    cap = cfg.capacity
+    g = torch.Generator(device="cuda").manual_seed(n_q)
+    qv = (torch.randn(n_q, cfg.n_q_heads, cfg.head_dim, generator=g, device="cuda") * 1.5
+          ).bfloat16()
+    for t in (cfg.ctx, cfg.ctx + 31):
+        seq = torch.tensor([t], dtype=torch.int32, device="cuda")
+        out = lib.std_dense_verify_attn_dlen(qv, lay["k"], lay["v"], cap, seq, n_q)
+        torch.cuda.synchronize()
+        ref = oracle.dense_verify(f64(qv), kf, vf, t + n_q)
+        say(f"n_q={n_q} t={t}: dense err {max_abs(f64(out), ref):.2e}")
+        assert max_abs(f64(out), ref) <= TOL
+
+
 def test_dlen_at_the_bound_equals_host_length(lib, c2):
     """With the device length equal to the bound the launch is the host-length
     launch: results are bitwise equal."""

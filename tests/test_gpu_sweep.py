@@ -86,6 +86,9 @@ def test_sweep_draws_cover_the_corners():
     assert any(c["topk"] == c["vis_len"] > 1 for c in cases)
     assert any(c["topk"] == 1 < c["vis_len"] for c in cases)
     assert any(c["vis_len"] < 9 for c in cases) and any(c["n_gen"] == 0 for c in cases)
+    # verify groups past 64 query rows at head_dim 128 (128-row workgroups)
+    assert any(c["d"] == 128 and c["dtype"] == "bf16" and c["n_q"] * c["hq"] // c["hkv"] > 64
+               for c in cases)
 
 
 @pytest.mark.gpu
